@@ -1,0 +1,279 @@
+/*
+ * arnfp8_oracle.c -- plain, slow, single-threaded CPU oracle for the fused
+ * all-reduce sum + residual + RMSNorm + per-row dynamic FP8 quantisation
+ * epilogue.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this code.  It shares nothing
+ * with the GPU path.  Build: gcc -O2 -std=c11 -ffp-contract=off (no fast-math:
+ * every fp32 operation below must be one IEEE-754 rounding in the order shown).
+ *
+ * What the operation computes, and where it comes from:
+ *  - Sum of the per-GPU input buffers, then RMSNorm with gamma and an additive
+ *    weight offset and epsilon, then FP8 dynamic quantisation with one fp32
+ *    scale per row (last dim 1), the scale bounded above by scale_ub:
+ *    Modular Mojo API docs, "allreduce_rmsnorm_fp8" (function summary; Args:
+ *    input_buffers, output, gamma, epsilon, weight_offset, scale_ub,
+ *    scale_output).
+ *  - The sum is accumulated in fp32 in a fixed rank order and rounded to bf16
+ *    once: b12x PR #283 "PCIeTwoShotBF16" (PR description; Validation,
+ *    "Precision").
+ *  - A residual is added before the norm and the updated residual is written
+ *    back (the RESIDUAL_RMS_NORM epilogue): TensorRT-LLM PR #19836
+ *    (Description).
+ *  - weight_offset = 1 gives the unit-offset gain 1 + gamma: tt-metal
+ *    rmsnorm_2d.py (RMSNorm2DConfig.add_unit_offset, "e.g., for Gemma").
+ *  - Per-row ("per-token") dynamic quantisation to E4M3FN / E5M2: Huawei CANN
+ *    aclnnAlltoAllQuantMatmul (x1QuantMode, x1QuantDtype).
+ *
+ * Readings where the pages are silent (each one is listed in the design
+ * notes): the residual adds the *rounded* bf16 sum; the norm reads the rounded
+ * bf16 h; the fp32 accumulator starts from rank 0's value (so -0 survives
+ * P = 1); gamma + weight_offset is one fp32 add (not re-rounded to bf16); eps
+ * is added to the mean square inside the square root; amax is taken over the
+ * post-gain normalised row; the fp8 code is decided from an fp32 value
+ * (fl32(y / scale)), round-to-nearest-even with saturation at +-448.
+ *
+ * The norm statistics and the normalised row are computed in fp64, so the
+ * oracle's y is the exact value up to a few fp64 roundings.
+ */
+#include "arnfp8_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- bf16 -- */
+
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16; /* bf16 is the top half of an fp32 */
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if (isnan(f))
+        return (uint16_t)((u >> 16) | 0x0040u); /* keep sign, force quiet */
+
+    /* The kept half truncates toward zero; the dropped half decides.  More
+     * than half an ulp -> away from zero; exactly half -> to the even kept
+     * half.  A carry out of the mantissa correctly bumps the exponent (and
+     * the largest finite values overflow to inf, as rounding demands). */
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))
+        kept += 1u;
+    return (uint16_t)kept;
+}
+
+/* ------------------------------------------------------ small floats -- */
+/*
+ * A sign-magnitude binary float with E exponent bits, M mantissa bits and
+ * exponent bias B.  e4m3fn: E=4, M=3, B=7, top code 0x7F is NaN, no inf, max
+ * finite 1.75 * 2^8 = 448.  e5m2: E=5, M=2, B=15, IEEE-like (inf and NaN in
+ * the top exponent), max finite 1.75 * 2^15 = 57344.
+ */
+
+/* Round a non-negative finite magnitude to the nearest multiple of the
+ * format's spacing at that magnitude, ties to the even multiple.  `emin` is
+ * the exponent of the smallest normal number and `mbits` the mantissa width;
+ * below 2^emin the spacing stays 2^(emin - mbits) (subnormals). */
+static double round_to_grid(double a, int emin, int mbits)
+{
+    int e;
+    if (a < ldexp(1.0, emin)) {
+        e = emin;
+    } else {
+        int k;
+        (void)frexp(a, &k); /* a = m * 2^k, m in [0.5, 1) */
+        e = k - 1;          /* a in [2^e, 2^(e+1)) */
+    }
+    double quantum = ldexp(1.0, e - mbits);
+    double n = a / quantum; /* exact: division by a power of two */
+    double lo = floor(n);
+    double frac = n - lo;
+    if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) == 1.0))
+        lo += 1.0;
+    return lo * quantum; /* may be 2^(e+1): the next binade, still exact */
+}
+
+/* Bit pattern of a non-negative value that is exactly representable. */
+static uint8_t encode_exact(double v, int emin, int mbits, int bias)
+{
+    if (v == 0.0)
+        return 0;
+    if (v < ldexp(1.0, emin)) { /* subnormal: exponent field 0 */
+        double m = v / ldexp(1.0, emin - mbits);
+        return (uint8_t)m;
+    }
+    int k;
+    double m = frexp(v, &k);    /* v = m * 2^k, m in [0.5, 1) */
+    int e = k - 1;              /* v = (2m) * 2^e, 2m in [1, 2) */
+    double frac = (2.0 * m - 1.0) * ldexp(1.0, mbits);
+    return (uint8_t)(((e + bias) << mbits) | (int)frac);
+}
+
+static double decode_small(uint8_t code, int ebits, int mbits, int bias)
+{
+    int sign = (code >> (ebits + mbits)) & 1;
+    int efield = (code >> mbits) & ((1 << ebits) - 1);
+    int mfield = code & ((1 << mbits) - 1);
+    double v;
+    if (efield == 0)
+        v = ldexp((double)mfield, 1 - bias - mbits);
+    else
+        v = ldexp(1.0 + ldexp((double)mfield, -mbits), efield - bias);
+    return sign ? -v : v;
+}
+
+double oracle_e4m3fn_to_f64(uint8_t code)
+{
+    if ((code & 0x7F) == 0x7F)
+        return NAN; /* S.1111.111 is the only NaN; there is no inf */
+    return decode_small(code, 4, 3, 7);
+}
+
+uint8_t oracle_f32_to_e4m3fn_sat(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0)
+        return sign | 0x7E; /* saturate at the largest finite value */
+    double r = round_to_grid(a, -6, 3); /* a < 448 rounds to at most 448 */
+    return sign | encode_exact(r, -6, 3, 7);
+}
+
+double oracle_e5m2_to_f64(uint8_t code)
+{
+    int efield = (code >> 2) & 0x1F;
+    if (efield == 0x1F) {
+        if (code & 0x3)
+            return NAN;
+        return (code & 0x80) ? -INFINITY : INFINITY;
+    }
+    return decode_small(code, 5, 2, 15);
+}
+
+uint8_t oracle_f32_to_e5m2_sat(float v)
+{
+    if (isnan(v))
+        return 0x7E;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 57344.0)
+        return sign | 0x7B; /* saturate at the largest finite value */
+    double r = round_to_grid(a, -14, 2); /* a < 57344 rounds to <= 57344 */
+    return sign | encode_exact(r, -14, 2, 15);
+}
+
+/* ------------------------------------------------------ the operation -- */
+
+static int check_common(const uint16_t *const *inputs, int P, int64_t rows,
+                        int64_t cols)
+{
+    if (inputs == NULL || P < 1 || P > 8 || rows < 0 || cols <= 0)
+        return ORACLE_BAD_ARG;
+    for (int p = 0; p < P; ++p)
+        if (inputs[p] == NULL)
+            return ORACLE_BAD_ARG;
+    return ORACLE_OK;
+}
+
+/* One element of the rank-order sum: start from rank 0's value, add ranks
+ * 1..P-1 in order, each add one fp32 rounding; round the total to bf16 once. */
+static uint16_t rank_order_sum(const uint16_t *const *inputs, int P, int64_t k)
+{
+    float acc = oracle_bf16_to_f32(inputs[0][k]);
+    for (int p = 1; p < P; ++p)
+        acc = acc + oracle_bf16_to_f32(inputs[p][k]);
+    return oracle_f32_to_bf16(acc);
+}
+
+int oracle_sum_bf16(const uint16_t *const *inputs, int P, uint16_t *out,
+                    int64_t rows, int64_t cols)
+{
+    int st = check_common(inputs, P, rows, cols);
+    if (st != ORACLE_OK || out == NULL)
+        return st != ORACLE_OK ? st : ORACLE_BAD_ARG;
+    for (int64_t k = 0; k < rows * cols; ++k)
+        out[k] = rank_order_sum(inputs, P, k);
+    return ORACLE_OK;
+}
+
+int oracle_arnfp8(const uint16_t *const *inputs, int P,
+                  const uint16_t *residual_in, uint16_t *residual_out,
+                  uint8_t *out_fp8, float *scales, const uint16_t *gamma,
+                  float eps, float weight_offset, float scale_ub,
+                  int64_t rows, int64_t cols)
+{
+    int st = check_common(inputs, P, rows, cols);
+    if (st != ORACLE_OK)
+        return st;
+    if (out_fp8 == NULL || scales == NULL || gamma == NULL)
+        return ORACLE_BAD_ARG;
+
+    double *h = (double *)malloc((size_t)cols * sizeof(double));
+    double *y = (double *)malloc((size_t)cols * sizeof(double));
+    if (h == NULL || y == NULL) {
+        free(h);
+        free(y);
+        return ORACLE_NO_MEMORY;
+    }
+
+    for (int64_t i = 0; i < rows; ++i) {
+        /* Sum, optional residual add, residual write-back. */
+        for (int64_t j = 0; j < cols; ++j) {
+            int64_t k = i * cols + j;
+            uint16_t hb = rank_order_sum(inputs, P, k);
+            if (residual_in != NULL) {
+                float t = oracle_bf16_to_f32(hb) + oracle_bf16_to_f32(residual_in[k]);
+                hb = oracle_f32_to_bf16(t);
+            }
+            if (residual_out != NULL)
+                residual_out[k] = hb;
+            h[j] = (double)oracle_bf16_to_f32(hb);
+        }
+
+        /* RMSNorm: r = 1 / sqrt(mean(h^2) + eps), y = h * r * g. */
+        double sumsq = 0.0;
+        for (int64_t j = 0; j < cols; ++j)
+            sumsq += h[j] * h[j];
+        double ms = sumsq / (double)cols;
+        double r = 1.0 / sqrt(ms + (double)eps);
+
+        double ymax = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            float g = oracle_bf16_to_f32(gamma[j]) + weight_offset; /* fp32 add */
+            y[j] = h[j] * r * (double)g;
+            if (fabs(y[j]) > ymax)
+                ymax = fabs(y[j]);
+        }
+
+        /* Per-row scale: amax clamped at scale_ub, over the e4m3fn maximum,
+         * floored at 1 / (448 * 512); all in fp32. */
+        float amax = (float)ymax;
+        float scale = fmaxf(fminf(amax, scale_ub) / 448.0f, 1.0f / 229376.0f);
+        scales[i] = scale;
+
+        /* Quantise: the code is decided from the fp32 value y / scale. */
+        for (int64_t j = 0; j < cols; ++j) {
+            float v = (float)(y[j] / (double)scale);
+            if (v > 448.0f)
+                v = 448.0f;
+            if (v < -448.0f)
+                v = -448.0f;
+            out_fp8[i * cols + j] = oracle_f32_to_e4m3fn_sat(v);
+        }
+    }
+
+    free(h);
+    free(y);
+    return ORACLE_OK;
+}

@@ -1,0 +1,81 @@
+/*
+ * arnfp8_oracle.h -- CPU oracle for the fused all-reduce sum + residual + RMSNorm
+ * + per-row dynamic FP8 (e4m3fn) quantisation epilogue.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library.  The GPU product
+ * path shares no code, header, table or helper with it.
+ *
+ * Number formats at this interface:
+ *   bf16    -> uint16_t bit patterns
+ *   e4m3fn  -> uint8_t  bit patterns (OCP FP8 E4M3, bias 7, max 448, no inf)
+ *   e5m2    -> uint8_t  bit patterns (OCP FP8 E5M2, bias 15, max 57344, has inf)
+ *   fp32    -> float
+ * All tensors are dense row-major [rows, cols]; every call is single-threaded,
+ * synchronous, and writes only the outputs it is given.
+ */
+#ifndef ARNFP8_ORACLE_H
+#define ARNFP8_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- number-format codecs --------------------------------------------- */
+
+/* bf16 -> fp32: the bf16 pattern is the upper half of the fp32 pattern. */
+float oracle_bf16_to_f32(uint16_t b);
+
+/* fp32 -> bf16, round to nearest, ties to even.  NaN stays NaN (quieted). */
+uint16_t oracle_f32_to_bf16(float f);
+
+/* e4m3fn code -> its exact value (NaN for 0x7F / 0xFF). */
+double oracle_e4m3fn_to_f64(uint8_t code);
+
+/* fp32 -> e4m3fn: round to nearest, ties to even, saturating at +-448.
+ * NaN -> 0x7F. */
+uint8_t oracle_f32_to_e4m3fn_sat(float v);
+
+/* e5m2 code -> its exact value (+-inf for 0x7C / 0xFC, NaN above). */
+double oracle_e5m2_to_f64(uint8_t code);
+
+/* fp32 -> e5m2: round to nearest, ties to even, saturating at +-57344.
+ * NaN -> 0x7E. */
+uint8_t oracle_f32_to_e5m2_sat(float v);
+
+/* ---- the operation ------------------------------------------------------ */
+
+/* Status codes returned by the oracle entry points. */
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEMORY 2
+
+/* Rank-order sum: out = bf16_rne(((x_0 + x_1) + x_2) + ... + x_{P-1}) with every
+ * add in fp32 and x_p the exact fp32 value of inputs[p].  P in [1, 8]. */
+int oracle_sum_bf16(const uint16_t *const *inputs, int P, uint16_t *out,
+                    int64_t rows, int64_t cols);
+
+/* The fused epilogue, per row i:
+ *   s   = rank-order sum (as oracle_sum_bf16)
+ *   h   = bf16_rne(fp32(s) + fp32(residual_in)) if residual_in, else s
+ *   residual_out <- h (if residual_out; may equal residual_in)
+ *   g_j = fl32(fp32(gamma_j) + weight_offset)
+ *   r   = 1 / sqrt(mean_j(h_j^2) + eps)                          (fp64)
+ *   y_j = h_j * r * g_j                                           (fp64)
+ *   amax = fl32(max_j |y_j|)
+ *   scale = max(min(amax, scale_ub) / 448, 1 / (448 * 512))        (fp32)
+ *   q_j = e4m3fn_rne_sat(fl32(y_j / scale))
+ * scales[i] = scale.  out_fp8 holds the q codes. */
+int oracle_arnfp8(const uint16_t *const *inputs, int P,
+                  const uint16_t *residual_in, uint16_t *residual_out,
+                  uint8_t *out_fp8, float *scales, const uint16_t *gamma,
+                  float eps, float weight_offset, float scale_ub,
+                  int64_t rows, int64_t cols);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARNFP8_ORACLE_H */
