@@ -1,0 +1,132 @@
+"""Thin Python binding of ``libarnfp8.so``, the gfx950 fused all-reduce epilogue.
+
+Every entry point here has the C ABI's name and argument order and does only
+argument marshalling: tensors become device pointers, the stream becomes the
+current PyTorch stream's handle, and a non-zero status raises ``ArnFp8Error``.
+All arithmetic runs in the library's HIP kernels; there is no CPU fallback --
+if the library is not built, every call raises.
+
+PyTorch is used for device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "ArnFp8Error", "MAX_P", "MAX_COLS", "STATUS",
+    "arnfp8_run", "arn_sum_bf16", "arnfp8_status_string", "library", "library_path",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libarnfp8.so")
+
+MAX_P = 8
+MAX_COLS = 65536
+STATUS = {
+    0: "ARNFP8_OK", 1: "ARNFP8_NULL_POINTER", 2: "ARNFP8_MISALIGNED", 3: "ARNFP8_BAD_SHAPE",
+    4: "ARNFP8_BAD_P", 5: "ARNFP8_ALIAS", 6: "ARNFP8_HIP_ERROR", 7: "ARNFP8_BAD_CONFIG",
+}
+
+
+class ArnFp8Error(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({arnfp8_status_string(status)})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libarnfp8.so`` (built in-tree by ``all_reduce_rmsnorm_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                f"{_LIB_PATH} is not built; run `python -m all_reduce_rmsnorm_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.arnfp8_run.restype = ctypes.c_int
+        L.arnfp8_run.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
+                                 ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int, vp]
+        L.arn_sum_bf16.restype = ctypes.c_int
+        L.arn_sum_bf16.argtypes = [ctypes.POINTER(vp), vp, i64, i64, ctypes.c_int, vp]
+        L.arnfp8_status_string.restype = ctypes.c_char_p
+        L.arnfp8_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device pointer of a tensor (or a raw integer address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ptr_array(inputs):
+    ptrs = [_ptr(x) for x in inputs]
+    return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _shape(inputs, rows, cols, P):
+    if P is None:
+        P = len(inputs)
+    if (rows is None or cols is None) and len(inputs) > 0 and hasattr(inputs[0], "shape"):
+        shp = inputs[0].shape
+        if cols is None:
+            cols = int(shp[-1])
+        if rows is None:
+            rows = int(inputs[0].numel() // shp[-1]) if shp[-1] else 0
+    return int(rows), int(cols), int(P)
+
+
+def arnfp8_status_string(status: int) -> str:
+    return library().arnfp8_status_string(int(status)).decode()
+
+
+def arnfp8_run(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps, weight_offset,
+               scale_ub, rows=None, cols=None, P=None, stream=None) -> None:
+    """The fused epilogue (sum, residual, RMSNorm, per-row e4m3fn quant), one launch.
+
+    ``inputs``: sequence of P bf16 [rows, cols] device tensors in rank order.
+    ``residual_in`` / ``residual_out``: bf16 [rows, cols] or None (may be the same tensor).
+    ``out_fp8``: e4m3fn (or uint8) [rows, cols]; ``scales``: fp32 [rows] or [rows, 1];
+    ``gamma``: bf16 [cols].  ``rows``, ``cols``, ``P`` default to the inputs' shape.
+    Runs on ``stream`` (default: PyTorch's current stream).
+    """
+    rows, cols, P = _shape(inputs, rows, cols, P)
+    st = library().arnfp8_run(_ptr_array(inputs), _ptr(residual_in), _ptr(residual_out),
+                              _ptr(out_fp8), _ptr(scales), _ptr(gamma), float(eps),
+                              float(weight_offset), float(scale_ub), rows, cols, P,
+                              _stream(stream))
+    if st != 0:
+        raise ArnFp8Error("arnfp8_run", st)
+
+
+def arn_sum_bf16(inputs, out, rows=None, cols=None, P=None, stream=None) -> None:
+    """Rank-order fp32 sum of P bf16 slabs, rounded once to bf16, into ``out``."""
+    rows, cols, P = _shape(inputs, rows, cols, P)
+    st = library().arn_sum_bf16(_ptr_array(inputs), _ptr(out), rows, cols, P, _stream(stream))
+    if st != 0:
+        raise ArnFp8Error("arn_sum_bf16", st)

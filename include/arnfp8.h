@@ -1,0 +1,112 @@
+/*
+ * arnfp8.h -- C ABI of the MI355X (gfx950) fused all-reduce epilogue library.
+ *
+ * One GPU holds P per-rank bf16 slabs in HBM, the packs a rank would pull from
+ * its peers.  The library sums them in fp32 in rank order and rounds once to
+ * bf16, optionally adds a bf16 residual and writes the updated residual back,
+ * applies RMSNorm with gain gamma + weight_offset, and quantises every row to
+ * fp8 e4m3fn with one dynamic fp32 scale per row -- all in one kernel launch.
+ *
+ * Sources for the operation:
+ *   - Modular Mojo API docs, "allreduce_rmsnorm_fp8" (function summary: the
+ *     all-reduce, RMSNorm and FP8 dynamic quantisation happen in a single
+ *     launch with no global-memory round trip between the reduction and the
+ *     norm; Args: input_buffers, output, gamma, epsilon, weight_offset,
+ *     scale_ub, scale_output).
+ *   - b12x PR #283 "PCIeTwoShotBF16" (PR description: fp32 accumulation in a
+ *     fixed rank order, one rounding to bf16, deterministic across calls and
+ *     graph replays).
+ *   - TensorRT-LLM PR #19836 (Description: the RESIDUAL_RMS_NORM epilogue --
+ *     residual add, residual write-back, RMSNorm).
+ *   - tt-metal rmsnorm_2d.py (RMSNorm2DConfig.add_unit_offset: gain 1 + gamma).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor is dense row-major, with no strides.  bf16 and fp8 tensors
+ *     are passed as untyped device pointers; fp32 tensors as float*.
+ *   - Device pointers must be 16-byte aligned (the kernels move 16-byte
+ *     vectors), except `scales`, which must be 4-byte aligned.
+ *   - `cols` must be a positive multiple of 8 and at most ARNFP8_MAX_COLS;
+ *     `rows` may be 0 (the call then does nothing and returns ARNFP8_OK).
+ *   - 1 <= P <= ARNFP8_MAX_P.  The host array `inputs` is read during the call
+ *     and its P pointers are passed by value to the kernel; the caller may
+ *     reuse the array as soon as the call returns.
+ *   - Ownership: the caller owns every buffer.  The library allocates nothing
+ *     and keeps no state between calls, so calls may be captured in a HIP
+ *     graph; pointers captured that way must stay valid for the graph's life.
+ *   - Validation happens on the host before any launch and touches no device
+ *     state; a call that returns an error has launched nothing.
+ *   - Execution is asynchronous on `stream` (NULL = the default stream);
+ *     results are visible to later work on that stream.  Results are
+ *     deterministic: bitwise identical on every call and every launch shape.
+ *   - Concurrent calls on different streams must not share output buffers.
+ *   - Non-finite inputs are not supported (the results are unspecified).
+ */
+#ifndef ARNFP8_H
+#define ARNFP8_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ARNFP8_MAX_P 8
+#define ARNFP8_MAX_COLS 65536
+
+/* Status codes. */
+#define ARNFP8_OK 0
+#define ARNFP8_NULL_POINTER 1 /* a required pointer is NULL                      */
+#define ARNFP8_MISALIGNED 2   /* a pointer breaks the alignment rule above       */
+#define ARNFP8_BAD_SHAPE 3    /* rows < 0, cols <= 0, cols % 8, cols too large,
+                                 or the byte size overflows int64              */
+#define ARNFP8_BAD_P 4        /* P outside [1, ARNFP8_MAX_P]                     */
+#define ARNFP8_ALIAS 5        /* an output overlaps an input or another output
+                                 (residual_out == residual_in is allowed)      */
+#define ARNFP8_HIP_ERROR 6    /* the launch failed (hipGetLastError)             */
+#define ARNFP8_BAD_CONFIG 7   /* an arnfp8_run_ex launch option is invalid       */
+
+/*
+ * arnfp8_run -- the fused epilogue.  For every row i and column j:
+ *   s    = bf16_rne(((x_0 + x_1) + ...) + x_{P-1}),   x_p = fp32(inputs[p][i,j]),
+ *          every add in fp32, in rank order (rank 0's value starts the sum)
+ *   h    = bf16_rne(fp32(s) + fp32(residual_in[i,j]))  if residual_in, else s
+ *   residual_out[i,j] = h                               if residual_out
+ *   g_j  = fp32(gamma[j]) + weight_offset                          (fp32)
+ *   r    = 1 / sqrt(sum_j h_j^2 / cols + eps)
+ *   amax = max_j |h_j * g_j| * r
+ *   scale = max(min(amax, scale_ub) / 448, 1 / (448 * 512))
+ *   out_fp8[i,j] = e4m3fn(clamp(h_j * g_j * r / scale, -448, 448)),
+ *          round to nearest even;  scales[i] = scale.
+ *
+ * inputs       host array of P device pointers, bf16 [rows, cols], rank order
+ * residual_in  device bf16 [rows, cols], or NULL (no residual add)
+ * residual_out device bf16 [rows, cols], or NULL; may equal residual_in
+ *              (in-place update).  With residual_in == NULL it receives s.
+ * out_fp8      device e4m3fn [rows, cols] (OCP FP8 E4M3: bias 7, max 448)
+ * scales       device fp32 [rows] (the [rows, 1] per-row scales)
+ * gamma        device bf16 [cols]
+ * eps, weight_offset, scale_ub   fp32 scalars, used as given
+ * Norm and scale arithmetic is fp32 with IEEE division and square root.
+ */
+int arnfp8_run(const void *const *inputs, const void *residual_in, void *residual_out,
+               void *out_fp8, float *scales, const void *gamma, float eps,
+               float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
+               hipStream_t stream);
+
+/*
+ * arn_sum_bf16 -- the reduction alone: out = s as defined for arnfp8_run.
+ * out is device bf16 [rows, cols] and must not overlap any input.
+ * Source: b12x PR #283 "PCIeTwoShotBF16" (PR description).
+ */
+int arn_sum_bf16(const void *const *inputs, void *out, int64_t rows, int64_t cols, int P,
+                 hipStream_t stream);
+
+/* Human-readable text for a status code (a static string; never NULL). */
+const char *arnfp8_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARNFP8_H */

@@ -1,0 +1,325 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs come from the seeded generators in ``all_reduce_rmsnorm_amd.synth``;
+the oracle sees the very same bytes.  Bar: bf16 bit-exact, scales within
+1e-5 relative, fp8 within one e4m3 step (see ``tests/_util.py``).
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests._util import assert_bits_equal, assert_fp8_close, assert_scales_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def arn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import all_reduce_rmsnorm_amd as arn
+
+    arn.library()
+    return arn
+
+
+@pytest.fixture(scope="module")
+def synth():
+    from all_reduce_rmsnorm_amd import synth
+
+    return synth
+
+
+def _bits(t):
+    from all_reduce_rmsnorm_amd import synth
+
+    return synth.bf16_bits(t)
+
+
+def _fp8(t):
+    from all_reduce_rmsnorm_amd import synth
+
+    return synth.fp8_bits(t)
+
+
+def run_fused(arn, inputs, gamma, eps, woff, ub, residual=None, in_place=True, want_res_out=True):
+    rows, cols = inputs[0].shape
+    out = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=DEV)
+    scales = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    res_out = None
+    if want_res_out:
+        if residual is not None and in_place:
+            res_out = residual
+        else:
+            res_out = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    arn.arnfp8_run(inputs, residual, res_out, out, scales, gamma, eps, woff, ub)
+    torch.cuda.synchronize()
+    return out, scales, res_out
+
+
+def check_against_oracle(orc, inputs_h, gamma_h, eps, woff, ub, res_h, out, scales, res_out,
+                         min_exact=0.999):
+    q_ref, s_ref, h_ref = orc.arnfp8([_bits(x) for x in inputs_h], _bits(gamma_h), eps, woff, ub,
+                                     residual_in=None if res_h is None else _bits(res_h))
+    if res_out is not None:
+        assert_bits_equal(_bits(res_out), h_ref, "residual_out")
+    assert_scales_close(scales.cpu().numpy(), s_ref)
+    assert_fp8_close(_fp8(out), q_ref, min_exact=min_exact)
+    return q_ref, s_ref, h_ref
+
+
+# ------------------------------------------------------------------ sum ----
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("rows,cols", [(1, 8), (3, 40), (37, 2880), (64, 4096), (5, 7176)])
+def test_sum_bf16_bit_exact(arn, orc, P, rows, cols):
+    print(f"[sum] P={P} rows={rows} cols={cols}", flush=True)
+    g = torch.Generator().manual_seed(1000 * P + rows)
+    xs = [(torch.randn((rows, cols), generator=g) * 3.0).to(torch.bfloat16) for _ in range(P)]
+    dev = [x.to(DEV) for x in xs]
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    arn.arn_sum_bf16(dev, out)
+    torch.cuda.synchronize()
+    assert_bits_equal(_bits(out), orc.sum_bf16([_bits(x) for x in xs]), "sum")
+
+
+def test_sum_workload_full_size(arn, orc, synth):
+    w = synth.WORKLOADS["sum_p4_64x4096"]
+    print(f"[sum] workload {w.name}", flush=True)
+    h = synth.make_inputs(w, device="cpu")
+    dev = [x.to(DEV) for x in h["inputs"]]
+    out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=DEV)
+    arn.arn_sum_bf16(dev, out)
+    torch.cuda.synchronize()
+    assert_bits_equal(_bits(out), orc.sum_bf16([_bits(x) for x in h["inputs"]]), "sum")
+
+
+def test_sum_negative_zero_and_ties(arn, orc):
+    # P = 1 keeps -0; exact half-ulp ties round to even.
+    vals = torch.tensor([[-0.0, 0.0, 16.0, 16.125, 1.0, -16.0, 8.0, 3.0]], dtype=torch.float32)
+    x = vals.to(torch.bfloat16)
+    out = torch.empty_like(x, device=DEV)
+    arn.arn_sum_bf16([x.to(DEV)], out)
+    torch.cuda.synchronize()
+    assert_bits_equal(_bits(out), _bits(x), "P=1 identity")
+    y = torch.tensor([[0.0, -0.0, 0.0625, 0.0625, 2.0 ** -8, -0.0625, 8.0, 2.0 ** -7]]).to(torch.bfloat16)
+    out2 = torch.empty_like(x, device=DEV)
+    arn.arn_sum_bf16([x.to(DEV), y.to(DEV)], out2)
+    torch.cuda.synchronize()
+    assert_bits_equal(_bits(out2), orc.sum_bf16([_bits(x), _bits(y)]), "ties")
+
+
+# ---------------------------------------------------------------- fused ----
+
+@pytest.mark.parametrize("name", ["tiny_p2_4x256", "decode_p4_32x7168", "unit_offset_p8_128x8192",
+                                  "prefill_share_p8_1024x7168"])
+def test_fused_workload_full_size(arn, orc, synth, name):
+    w = synth.WORKLOADS[name]
+    print(f"[fused] workload {w.name}", flush=True)
+    h = synth.make_inputs(w, device="cpu")
+    dev = [x.to(DEV) for x in h["inputs"]]
+    res = None if h["residual"] is None else h["residual"].to(DEV)
+    out, scales, res_out = run_fused(arn, dev, h["gamma"].to(DEV), w.eps, w.weight_offset,
+                                     w.scale_ub, residual=res, in_place=True)
+    check_against_oracle(orc, h["inputs"], h["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                         h["residual"], out, scales, res_out)
+
+
+def test_fused_prefill_full_size_sampled_rows(arn, orc, synth):
+    """The prefill workload at its full size, generated on the GPU; the oracle
+    checks a seeded sample of rows, and size-free properties cover every row."""
+    w = synth.WORKLOADS["prefill_p8_8192x7168"]
+    print(f"[fused] workload {w.name} (sampled rows)", flush=True)
+    d = synth.make_inputs(w, device=DEV)
+    res0 = d["residual"].clone()
+    out, scales, res_out = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset,
+                                     w.scale_ub, residual=d["residual"], in_place=True)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, w.rows - 1], rng.choice(w.rows, 253, replace=False)]))
+    idx = torch.from_numpy(rows).to(DEV)
+    xs_h = [x.index_select(0, idx).cpu() for x in d["inputs"]]
+    q_ref, s_ref, h_ref = orc.arnfp8([_bits(x) for x in xs_h], _bits(d["gamma"].cpu()), w.eps,
+                                     w.weight_offset, w.scale_ub,
+                                     residual_in=_bits(res0.index_select(0, idx).cpu()))
+    assert_bits_equal(_bits(res_out.index_select(0, idx)), h_ref, "residual_out")
+    assert_scales_close(scales.index_select(0, idx).cpu().numpy(), s_ref)
+    assert_fp8_close(_fp8(out.index_select(0, idx)), q_ref)
+    clamp = np.float32(w.scale_ub / 448.0)
+    assert (s_ref == clamp).sum() > 0, "the sample should contain rows where scale_ub clamps"
+    # every row: scales within [floor, ub/448]; every row reaches +-448
+    s_all = scales.cpu().numpy()
+    assert np.all(s_all <= clamp) and np.all(s_all >= np.float32(1.0 / 229376.0))
+    mags = (out.view(torch.uint8) & 0x7F).amax(dim=1).cpu().numpy()
+    assert np.all(mags == 0x7E)
+
+
+P2_COLS = [8, 2880, 7168, 7176, 8192, 16384]
+P2_ROWS = [1, 32, 37, 64]
+
+
+@pytest.mark.parametrize("cols", P2_COLS)
+@pytest.mark.parametrize("rows", P2_ROWS)
+def test_fused_shape_menu(arn, orc, rows, cols):
+    """Hidden sizes and token counts of TensorRT-LLM PR #19836's test set."""
+    P = 4 if cols % 16 == 0 else 2
+    print(f"[fused] menu P={P} rows={rows} cols={cols}", flush=True)
+    g = torch.Generator().manual_seed(rows * 100003 + cols)
+    xs = [(torch.randn((rows, cols), generator=g) * 0.5).to(torch.bfloat16) for _ in range(P)]
+    res = torch.randn((rows, cols), generator=g).to(torch.bfloat16)
+    gamma = (torch.rand((cols,), generator=g) * 0.4 + 0.8).to(torch.bfloat16)
+    out, scales, res_out = run_fused(arn, [x.to(DEV) for x in xs], gamma.to(DEV), 1e-6, 0.0,
+                                     1200.0, residual=res.to(DEV), in_place=False)
+    check_against_oracle(orc, xs, gamma, 1e-6, 0.0, 1200.0, res, out, scales, res_out,
+                         min_exact=0.99 if rows * cols < 4096 else 0.999)
+
+
+@pytest.mark.parametrize("P", [1, 3, 5, 6, 7, 8])
+@pytest.mark.parametrize("res_mode", ["none", "out_only", "in_only", "in_out"])
+def test_fused_every_p_and_residual_mode(arn, orc, P, res_mode):
+    rows, cols = 9, 1000  # 125 chunks per row: a ragged last wave
+    print(f"[fused] P={P} residual={res_mode}", flush=True)
+    g = torch.Generator().manual_seed(P * 7 + len(res_mode))
+    xs = [torch.randn((rows, cols), generator=g).to(torch.bfloat16) for _ in range(P)]
+    gamma = (torch.randn((cols,), generator=g) * 0.1 + 1.0).to(torch.bfloat16)
+    res = torch.randn((rows, cols), generator=g).to(torch.bfloat16)
+    res_in = res.to(DEV) if res_mode in ("in_only", "in_out") else None
+    want_out = res_mode in ("out_only", "in_out")
+    out, scales, res_out = run_fused(arn, [x.to(DEV) for x in xs], gamma.to(DEV), 1e-5, 0.0,
+                                     1200.0, residual=res_in, in_place=False,
+                                     want_res_out=want_out)
+    check_against_oracle(orc, xs, gamma, 1e-5, 0.0, 1200.0,
+                         res if res_in is not None else None, out, scales, res_out, min_exact=0.99)
+
+
+# ---------------------------------------------------------- edge cases ----
+
+def test_rows_zero_is_a_noop(arn):
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((0, 64), dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.empty((0,), dtype=torch.float32, device=DEV)
+    g = torch.ones((64,), dtype=torch.bfloat16, device=DEV)
+    arn.arnfp8_run([x, x], None, None, out, s, g, 1e-6, 0.0, 1.0, rows=0, cols=64)
+    arn.arn_sum_bf16([x], torch.empty_like(x), rows=0, cols=64)
+    torch.cuda.synchronize()
+
+
+def test_max_cols(arn, orc):
+    rows, cols = 3, 65536
+    g = torch.Generator().manual_seed(5)
+    xs = [torch.randn((rows, cols), generator=g).to(torch.bfloat16) for _ in range(8)]
+    gamma = (torch.rand((cols,), generator=g) + 0.5).to(torch.bfloat16)
+    res = torch.randn((rows, cols), generator=g).to(torch.bfloat16)
+    out, scales, res_out = run_fused(arn, [x.to(DEV) for x in xs], gamma.to(DEV), 1e-6, 0.0,
+                                     1200.0, residual=res.to(DEV), in_place=True)
+    check_against_oracle(orc, xs, gamma, 1e-6, 0.0, 1200.0, res, out, scales, res_out)
+
+
+def test_zero_and_tiny_rows_take_the_floor(arn, orc):
+    rows, cols = 4, 512
+    x = torch.zeros((rows, cols), dtype=torch.bfloat16)
+    x[2] = 2.0 ** -20
+    x[3, 7] = -(2.0 ** -30)
+    gamma = torch.ones((cols,), dtype=torch.bfloat16)
+    out, scales, res_out = run_fused(arn, [x.to(DEV), x.to(DEV)], gamma.to(DEV), 1.0, 0.0, 1200.0)
+    check_against_oracle(orc, [x, x], gamma, 1.0, 0.0, 1200.0, None, out, scales, res_out,
+                         min_exact=0.99)
+    assert np.all(scales.cpu().numpy() == np.float32(1.0 / 229376.0))
+
+
+def test_scale_clamps_exactly_at_ub(arn, orc):
+    rows, cols = 16, 2048
+    g = torch.Generator().manual_seed(6)
+    xs = [torch.randn((rows, cols), generator=g).to(torch.bfloat16) for _ in range(4)]
+    gamma = (torch.rand((cols,), generator=g) * 0.4 + 0.8).to(torch.bfloat16)
+    ub = 2.5
+    out, scales, res_out = run_fused(arn, [x.to(DEV) for x in xs], gamma.to(DEV), 1e-6, 0.0, ub)
+    _, s_ref, _ = check_against_oracle(orc, xs, gamma, 1e-6, 0.0, ub, None, out, scales, res_out)
+    s = scales.cpu().numpy()
+    clamped = s_ref == np.float32(ub / 448.0)
+    assert clamped.all()
+    assert np.all(s == np.float32(ub / 448.0))
+
+
+def test_unit_gain_bitwise(arn):
+    """gamma = 0 with weight_offset = 1 equals gamma = 1 with weight_offset = 0."""
+    rows, cols = 64, 8192
+    g = torch.Generator().manual_seed(7)
+    xs = [(torch.randn((rows, cols), generator=g) * 0.25).to(torch.bfloat16).to(DEV) for _ in range(8)]
+    res = torch.randn((rows, cols), generator=g).to(torch.bfloat16).to(DEV)
+    a = run_fused(arn, xs, torch.zeros(cols, dtype=torch.bfloat16, device=DEV), 1e-5, 1.0, 1200.0,
+                  residual=res, in_place=False)
+    b = run_fused(arn, xs, torch.ones(cols, dtype=torch.bfloat16, device=DEV), 1e-5, 0.0, 1200.0,
+                  residual=res, in_place=False)
+    assert torch.equal(a[0].view(torch.uint8), b[0].view(torch.uint8))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_repeat_calls_bitwise_deterministic(arn, synth):
+    w = synth.WORKLOADS["unit_offset_p8_128x8192"]
+    d = synth.make_inputs(w, device=DEV)
+    first = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                      residual=d["residual"], in_place=False)
+    for _ in range(5):
+        again = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                          residual=d["residual"], in_place=False)
+        assert torch.equal(first[0].view(torch.uint8), again[0].view(torch.uint8))
+        assert torch.equal(first[1], again[1]) and torch.equal(first[2], again[2])
+
+
+def test_graph_replay_matches_eager(arn, synth):
+    """Capture one fused call in a graph; every replay (with eager work and a
+    synchronisation between replays) equals the eager result bitwise."""
+    w = synth.WORKLOADS["decode_p4_32x7168"]
+    d = synth.make_inputs(w, device=DEV)
+    eager = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                      residual=d["residual"], in_place=False)
+    out = torch.empty_like(eager[0])
+    scales = torch.empty_like(eager[1])
+    res_out = torch.empty_like(eager[2])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the side stream, as graph capture asks
+        arn.arnfp8_run(d["inputs"], d["residual"], res_out, out, scales, d["gamma"], w.eps,
+                       w.weight_offset, w.scale_ub)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        arn.arnfp8_run(d["inputs"], d["residual"], res_out, out, scales, d["gamma"], w.eps,
+                       w.weight_offset, w.scale_ub)
+    for k in range(3):
+        out.view(torch.uint8).fill_(0x7F)
+        scales.fill_(-1.0)
+        res_out.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), eager[0].view(torch.uint8)), k
+        assert torch.equal(scales, eager[1]) and torch.equal(res_out, eager[2]), k
+        _ = (d["inputs"][0].float() * 2.0).sum().item()  # unrelated eager work between replays
+
+
+def test_in_place_residual_matches_out_of_place(arn, synth):
+    w = synth.WORKLOADS["decode_p4_32x7168"]
+    d = synth.make_inputs(w, device=DEV)
+    res_copy = d["residual"].clone()
+    a = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                  residual=res_copy, in_place=False)
+    b = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                  residual=d["residual"], in_place=True)
+    assert torch.equal(a[0].view(torch.uint8), b[0].view(torch.uint8))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_errors_raise_before_launch(arn):
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((4, 64), dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.empty((4,), dtype=torch.float32, device=DEV)
+    g = torch.ones((64,), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(arn.ArnFp8Error) as e:
+        arn.arnfp8_run([x, x], None, x, out, s, g, 1e-6, 0.0, 1.0)  # residual_out aliases inputs
+    assert e.value.status == 5
+    with pytest.raises(arn.ArnFp8Error) as e:
+        arn.arnfp8_run([x[:, 4:]], None, None, out, s, g, 1e-6, 0.0, 1.0, rows=4, cols=56)
+    assert e.value.status == 2
+    torch.cuda.synchronize()
