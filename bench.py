@@ -1,0 +1,409 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused sum + residual + RMSNorm + FP8 quant epilogue on one GPU.
+
+A step is one ``arnfp8_run`` call over the prefill workload (P = 8 bf16 slabs
+[8192, 7168] ~ N(0, 0.5) with 0.1 % outliers x100, bf16 residual ~ N(0, 1),
+gamma ~ U(0.8, 1.2), eps 1e-6, scale_ub 64), all inputs resident in HBM before
+the timed region.  Prints ONE JSON line:
+
+  value       algorithmic HBM bytes per step / wall time per step   (GB/s)
+  roofline    the kernel's algorithmic bytes / its average duration from HIP
+              events on the launch stream, against the 8 TB/s HBM peak; the
+              measured HBM traffic (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
+              by a plain copy of known size) when a committed counter summary
+              matches the current kernel source
+  cpu_baseline the CPU oracle on the same bytes (rows of the same workload)
+  latency_us_per_call  graph-replayed microseconds per call for the decode
+              shapes (P = 4 [32, 7168], P = 8 [128, 8192], P = 2 [4, 256])
+
+Other modes (not the JSON contract): ``--workload NAME`` times another
+workload; ``--pmc-calib`` first runs one plain copy of known size (the P = 1
+sum kernel; it scales the HBM counters); ``--summarize-pmc DIR`` turns rocprofv3 counter CSVs into the
+committed summary; ``--summarize-ktrace DIR`` does the same for a
+``rocprofv3 --kernel-trace --stats`` run.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+DEFAULT_WORKLOAD = "prefill_p8_8192x7168"
+DECODE_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "tiny_p2_4x256"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8.hip"),
+                  os.path.join(ROOT, "include", "arnfp8.h"),
+                  os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------- GPU side --
+
+def alloc_workload(w, torch, dev):
+    from all_reduce_rmsnorm_amd import synth
+
+    d = synth.make_inputs(w, device=dev)
+    rows, cols = w.rows, w.cols
+    d["out"] = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=dev)
+    d["scales"] = torch.empty((rows,), dtype=torch.float32, device=dev)
+    d["res_out"] = (torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+                    if d["residual"] is not None else None)
+    d["sum_out"] = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    return d
+
+
+def step_fn(w, d, arn):
+    if w.sum_only:
+        return lambda: arn.arn_sum_bf16(d["inputs"], d["sum_out"])
+    return lambda: arn.arnfp8_run(d["inputs"], d["residual"], d["res_out"], d["out"], d["scales"],
+                                  d["gamma"], w.eps, w.weight_offset, w.scale_ub)
+
+
+def time_steps(torch, fn, steps, warmup):
+    """Wall time of exactly `steps` calls (synchronised on both sides) and the
+    average per-launch duration from HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return wall / steps * 1e3, kern_ms
+
+
+def graph_us_per_call(torch, fn, calls=100, reps=5):
+    """Microseconds per call with `calls` calls captured in one graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    best = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        best.append(a.elapsed_time(b) * 1e3 / calls)
+    best.sort()
+    return best[len(best) // 2]
+
+
+# -------------------------------------------------------------- CPU side ---
+
+def cpu_baseline(w, d, torch, min_seconds=10.0, max_passes=3):
+    """The oracle over every row of the workload (same bytes as the GPU),
+    repeated until at least `min_seconds` of CPU work (at most `max_passes`)."""
+    import numpy as np
+
+    import oracle
+    from all_reduce_rmsnorm_amd import synth
+
+    block = 1024
+    gamma = synth.bf16_bits(d["gamma"])
+    total_t, passes = 0.0, 0
+    while passes < max_passes and (passes == 0 or total_t < min_seconds):
+        for r0 in range(0, w.rows, block):
+            r1 = min(w.rows, r0 + block)
+            xs = [synth.bf16_bits(x[r0:r1]) for x in d["inputs"]]
+            res = None if d["residual"] is None else synth.bf16_bits(d["residual"][r0:r1])
+            t = time.perf_counter()
+            if w.sum_only:
+                oracle.sum_bf16(xs)
+            else:
+                oracle.arnfp8(xs, gamma, w.eps, w.weight_offset, w.scale_ub, residual_in=res)
+            total_t += time.perf_counter() - t
+        passes += 1
+    per_pass = total_t / passes
+    return {
+        "value": round(w.algorithmic_bytes() / per_pass / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"every row of {w.name} ({w.rows} rows), {passes} pass(es), "
+                  f"{per_pass * 1e3:.1f} ms per pass; single-threaded C oracle",
+        "ms_per_step": round(per_pass * 1e3, 3),
+    }
+
+
+# ------------------------------------------------------- HBM counters ------
+
+def read_traffic(kernel_hash: str):
+    """(bytes per launch, note) from the committed counter summary, or None
+    when it is missing or was taken on different kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash:
+        return None
+    return int(m_bytes.group(1))
+
+
+def summarize_pmc(directory: str, out_path: str, workload: str):
+    """Build the counter summary from rocprofv3 --pmc CSV output under `directory`:
+    one run with FETCH_SIZE, one with WRITE_SIZE, each holding the fused kernel's
+    dispatches and one plain copy of known size (``--pmc-calib``)."""
+    import csv
+
+    from all_reduce_rmsnorm_amd import synth
+
+    w = synth.WORKLOADS[workload]
+    per = {}  # counter -> {"kernel": [kib...], "copy": [kib...]}
+    files = sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {directory}")
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            name = row.get("Kernel_Name", "")
+            ctr = row.get("Counter_Name", "")
+            val = float(row.get("Counter_Value", "nan"))
+            kind = "kernel" if "arnfp8_row_kernel" in name else (
+                "copy" if "arn_sum_kernel<1" in name else None)
+            if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
+                continue
+            per.setdefault(ctr, {}).setdefault(kind, []).append(val)
+    calib_bytes = int(os.environ.get("ARNFP8_CALIB_BYTES", str(1 << 30)))
+    lines = []
+    total = 0.0
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        k = per.get(ctr, {}).get("kernel", [])
+        c = per.get(ctr, {}).get("copy", [])
+        if not k or not c:
+            raise SystemExit(f"missing {ctr} samples (kernel {len(k)}, copy {len(c)})")
+        k_kib = sum(k) / len(k)
+        c_kib = max(c)
+        factor = calib_bytes / (c_kib * 1024.0)
+        scaled = k_kib * 1024.0 * factor
+        total += scaled
+        lines.append(f"| {ctr} | {k_kib:.0f} KiB ({len(k)} dispatches) | {c_kib:.0f} KiB | "
+                     f"{factor:.4f} | {scaled / 1e6:.2f} MB |")
+    alg = w.algorithmic_bytes()
+    text = "\n".join([
+        f"# HBM traffic of the fused row kernel on {w.name}",
+        "",
+        "Counters from two `rocprofv3 --pmc` runs (FETCH_SIZE, then WRITE_SIZE), per",
+        "dispatch, scaled by what the same counter reads for a plain copy of",
+        f"{calib_bytes} bytes (read {calib_bytes} B, write {calib_bytes} B).",
+        "Commands (from the repository root, on one MI355X):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+        "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-latency --pmc-calib",
+        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
+        "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-latency --pmc-calib",
+        "    python bench.py --summarize-pmc gpurun_out",
+        "",
+        "| counter | fused kernel (mean per dispatch) | copy kernel | scale factor | scaled bytes |",
+        "|---|---|---|---|---|",
+        *lines,
+        "",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        f"traffic_bytes_per_launch: {int(round(total))}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic / algorithmic: {total / alg:.4f}",
+        "",
+    ])
+    with open(out_path, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def _short_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0]
+
+
+def summarize_ktrace(directory: str, out_path: str, command: str):
+    """Summarise a rocprofv3 --kernel-trace --stats CSV run: the library's
+    kernels, split by launch shape (grid, workgroup), with mean durations."""
+    import csv
+    from collections import defaultdict
+
+    traces = sorted(glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True))
+    stats = sorted(glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True))
+    if not traces:
+        raise SystemExit(f"no kernel_trace.csv under {directory}")
+    shapes = defaultdict(list)
+    for f in traces:
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"]
+            if "arnfp8_" not in name and "arn_sum_kernel" not in name:
+                continue
+            key = (_short_name(name),
+                   int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            shapes[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = [f"# Kernel trace: {os.path.basename(out_path)[:-3]}", "",
+             "Command (from the repository root, on one MI355X):", "",
+             f"    {command}", "",
+             "Per launch shape (grid = total lanes), from the kernel trace:", "",
+             "| kernel | grid lanes | workgroup | calls | mean us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, grid, wg), v in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{name}` | {grid} | {wg} | {len(v)} | {sum(v) / len(v) / 1e3:.3f} | "
+                     f"{min(v) / 1e3:.3f} | {max(v) / 1e3:.3f} |")
+    if stats:
+        lines += ["", "rocprofv3 --stats summary (all kernels of the run, every shape pooled):", "",
+                  "| kernel | calls | mean us | share % |", "|---|---|---|---|"]
+        for r in csv.DictReader(open(stats[0])):
+            nm = _short_name(r["Name"])
+            if len(nm) > 90:
+                nm = nm[:87] + "..."
+            lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                         f"{float(r['Percentage']):.2f} |")
+    lines.append("")
+    text = "\n".join(lines)
+    with open(out_path, "w") as f:
+        f.write(text)
+    print(text)
+
+
+# -------------------------------------------------------------------- main --
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--pmc-calib", action="store_true",
+                    help="first run one plain device copy of 1 GiB (scales the HBM counters)")
+    ap.add_argument("--summarize-pmc", metavar="DIR")
+    ap.add_argument("--pmc-out", default=PMC_SUMMARY)
+    ap.add_argument("--summarize-ktrace", metavar="DIR")
+    ap.add_argument("--ktrace-out")
+    ap.add_argument("--ktrace-command", default="")
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.pmc_out, args.workload)
+        return 0
+    if args.summarize_ktrace:
+        summarize_ktrace(args.summarize_ktrace, args.ktrace_out, args.ktrace_command)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU exchange is out of scope; run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import all_reduce_rmsnorm_amd as arn
+    from all_reduce_rmsnorm_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    arn.library()
+
+    if args.pmc_calib:
+        # A plain copy of known size: the rank-order sum with P = 1 reads one
+        # bf16 tensor and writes it back unchanged (1 GiB each way).
+        src = torch.ones((65536, 8192), dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        arn.arn_sum_bf16([src], dst)
+        torch.cuda.synchronize()
+        log(f"pmc calibration copy: {src.numel() * 2} bytes read, {dst.numel() * 2} bytes written")
+        del src, dst
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"bench: workload {w.name}, steps {args.steps}, warmup {args.warmup}")
+    d = alloc_workload(w, torch, dev)
+    torch.cuda.synchronize()
+    fn = step_fn(w, d, arn)
+    ms_per_step, kern_ms = time_steps(torch, fn, args.steps, args.warmup)
+    alg = w.algorithmic_bytes()
+    value = alg / (ms_per_step * 1e-3) / 1e9
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    log(f"bench: {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events)")
+
+    khash = kernel_source_hash()
+    traffic = read_traffic(khash) if w.name == DEFAULT_WORKLOAD else None
+    result = {
+        "metric": "fused sum+RMSNorm+FP8 quant: achieved HBM GB/s (% of peak) and us/call",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtypes": "bf16 in, bf16 residual out, e4m3fn + f32 scales out" if not w.sum_only else "bf16 in, bf16 out",
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": w.name, "P": w.P, "rows": w.rows, "cols": w.cols,
+                   "residual": w.residual_std is not None, "eps": w.eps,
+                   "weight_offset": w.weight_offset, "scale_ub": w.scale_ub,
+                   "algorithmic_bytes_per_step": alg},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_us": round(kern_ms * 1e3, 3),
+                     "kernel_source_hash": khash},
+    }
+    if not args.no_latency:
+        lat = {}
+        for name in DECODE_WORKLOADS:
+            wd = synth.WORKLOADS[name]
+            dd = alloc_workload(wd, torch, dev)
+            lat[name] = round(graph_us_per_call(torch, step_fn(wd, dd, arn)), 3)
+            del dd
+        result["latency_us_per_call"] = lat
+        log(f"bench: graph-replayed latency {lat}")
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, d, torch)
+        log(f"bench: cpu baseline {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,169 @@
+"""Host-side checks of the C ABI library (no GPU needed, no kernel launched).
+
+The library must load, export every function ``include/arnfp8.h`` declares,
+and reject bad arguments with the documented status codes before touching
+the device.  Pointers below are fake addresses: validation reads none of them.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+OK, NULLP, MISALIGNED, BAD_SHAPE, BAD_P, ALIAS = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def L():
+    import all_reduce_rmsnorm_amd as arn
+
+    if not os.path.exists(arn.library_path()):
+        from all_reduce_rmsnorm_amd import build
+
+        build.build()
+    return arn.library()
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(HEADER_DIR, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\([^;{]*\)\s*;", text, flags=re.M):
+            names.append(m.group(1))
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("arnfp8_run", "arn_sum_bf16", "arnfp8_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} is declared in include/ but not exported"
+
+
+def test_library_is_built_for_gfx950():
+    """The offload bundle of the library built here names the gfx950 target."""
+    import all_reduce_rmsnorm_amd as arn
+
+    blob = open(arn.library_path(), "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+
+
+def test_status_strings(L):
+    import all_reduce_rmsnorm_amd as arn
+
+    for code in range(0, 8):
+        s = arn.arnfp8_status_string(code)
+        assert s and s != "unknown status"
+    assert arn.arnfp8_status_string(99) == "unknown status"
+
+
+def _arr(*ptrs):
+    return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+
+
+BASE = 1 << 40  # fake, well separated, 16-byte aligned addresses
+MB = 1 << 20
+
+
+def run(L, inputs, res_in=None, res_out=None, out=BASE + 100 * MB, scales=BASE + 200 * MB,
+        gamma=BASE + 300 * MB, rows=4, cols=256, P=None):
+    P = len(inputs) if P is None else P
+    return L.arnfp8_run(_arr(*inputs) if inputs is not None else None, res_in, res_out, out, scales,
+                        gamma, 1e-6, 0.0, 1.0, rows, cols, P, None)
+
+
+def test_fused_validation_codes(L):
+    x0, x1 = BASE, BASE + 10 * MB
+    assert run(L, [x0, x1], cols=255) == BAD_SHAPE
+    assert run(L, [x0, x1], cols=0) == BAD_SHAPE
+    assert run(L, [x0, x1], rows=-1) == BAD_SHAPE
+    assert run(L, [x0, x1], cols=65544) == BAD_SHAPE
+    assert run(L, [x0, x1], rows=1 << 62, cols=65536) == BAD_SHAPE
+    assert run(L, [x0, x1], P=0) == BAD_P
+    assert run(L, [x0] * 9) == BAD_P
+    assert run(L, None, P=2) == NULLP
+    assert run(L, [x0, None]) == NULLP
+    assert run(L, [x0, x1], out=None) == NULLP
+    assert run(L, [x0, x1], scales=None) == NULLP
+    assert run(L, [x0, x1], gamma=None) == NULLP
+    assert run(L, [x0 + 8, x1]) == MISALIGNED
+    assert run(L, [x0, x1], out=BASE + 100 * MB + 4) == MISALIGNED
+    assert run(L, [x0, x1], gamma=BASE + 300 * MB + 2) == MISALIGNED
+    assert run(L, [x0, x1], scales=BASE + 200 * MB + 2) == MISALIGNED
+    assert run(L, [x0, x1], res_in=BASE + 400 * MB + 8) == MISALIGNED
+
+
+def test_fused_alias_rules(L):
+    x0, x1 = BASE, BASE + 10 * MB
+    r = BASE + 400 * MB
+    n = 4 * 256
+    # (res_out == res_in is legal; it is not called here, as a legal call launches)
+    # outputs overlapping inputs
+    assert run(L, [x0, x1], out=x1 + 2 * n - 16) == ALIAS
+    assert run(L, [x0, x1], res_out=x0) == ALIAS
+    assert run(L, [x0, x1], scales=BASE + 300 * MB) == ALIAS  # scales on gamma
+    assert run(L, [x0, x1], res_in=r, res_out=r + 16) == ALIAS  # partial overlap with residual_in
+    # outputs overlapping each other
+    assert run(L, [x0, x1], res_out=BASE + 100 * MB) == ALIAS
+    assert run(L, [x0, x1], scales=BASE + 100 * MB + n - 4) == ALIAS
+
+
+def test_rows_zero_returns_ok_without_touching_anything(L):
+    assert run(L, [BASE, BASE + 10 * MB], rows=0, out=None, scales=None, gamma=None) == OK
+    assert L.arn_sum_bf16(_arr(BASE), None, 0, 64, 1, None) == OK
+
+
+def test_sum_validation_codes(L):
+    x0, x1 = BASE, BASE + 10 * MB
+    out = BASE + 100 * MB
+    assert L.arn_sum_bf16(_arr(x0, x1), out, 4, 12, 2, None) == BAD_SHAPE
+    assert L.arn_sum_bf16(_arr(x0, x1), out, 4, 64, 9, None) == BAD_P
+    assert L.arn_sum_bf16(_arr(x0, x1), None, 4, 64, 2, None) == NULLP
+    assert L.arn_sum_bf16(_arr(x0, x1), out + 2, 4, 64, 2, None) == MISALIGNED
+    assert L.arn_sum_bf16(_arr(x0, x1), x1 + 16, 4, 64, 2, None) == ALIAS
+
+
+def test_binding_raises_with_status(L):
+    import all_reduce_rmsnorm_amd as arn
+
+    with pytest.raises(arn.ArnFp8Error) as e:
+        arn.arn_sum_bf16([BASE, BASE + 10 * MB], BASE + 100 * MB, rows=4, cols=12, stream=0)
+    assert e.value.status == BAD_SHAPE
+
+
+def test_algorithmic_bytes_of_the_workloads():
+    from all_reduce_rmsnorm_amd import synth
+
+    W = synth.WORKLOADS
+    assert W["tiny_p2_4x256"].algorithmic_bytes() == 5648
+    assert W["sum_p4_64x4096"].algorithmic_bytes() == 2621440
+    assert W["decode_p4_32x7168"].algorithmic_bytes() == 2996352
+    assert W["unit_offset_p8_128x8192"].algorithmic_bytes() == 22036992
+    assert W["prefill_p8_8192x7168"].algorithmic_bytes() == 1233172480
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "all_reduce_rmsnorm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in re.sub(r"#.*|//.*", "", text).lower() or f == "synth.py", f
