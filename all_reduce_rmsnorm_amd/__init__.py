@@ -15,7 +15,8 @@ import os
 
 __all__ = [
     "ArnFp8Error", "MAX_P", "MAX_COLS", "STATUS",
-    "arnfp8_run", "arn_sum_bf16", "arnfp8_status_string", "library", "library_path",
+    "arnfp8_run", "arnfp8_run_ex", "arn_sum_bf16", "arnfp8_status_string", "Launch",
+    "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +36,17 @@ class ArnFp8Error(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn}: {STATUS.get(status, status)} ({arnfp8_status_string(status)})")
+
+
+VARIANT_AUTO = 0
+VARIANT_ROW = 1
+
+
+class Launch(ctypes.Structure):
+    """``arnfp8_launch``: launch options; 0 in a field means automatic."""
+
+    _fields_ = [("variant", ctypes.c_int), ("threads", ctypes.c_int), ("vpt", ctypes.c_int),
+                ("grid", ctypes.c_int)]
 
 
 _lib = None
@@ -57,6 +69,10 @@ def library() -> ctypes.CDLL:
         L.arnfp8_run.restype = ctypes.c_int
         L.arnfp8_run.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
                                  ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int, vp]
+        L.arnfp8_run_ex.restype = ctypes.c_int
+        L.arnfp8_run_ex.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
+                                    ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int, vp,
+                                    ctypes.POINTER(Launch)]
         L.arn_sum_bf16.restype = ctypes.c_int
         L.arn_sum_bf16.argtypes = [ctypes.POINTER(vp), vp, i64, i64, ctypes.c_int, vp]
         L.arnfp8_status_string.restype = ctypes.c_char_p
@@ -122,6 +138,22 @@ def arnfp8_run(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps, w
                               _stream(stream))
     if st != 0:
         raise ArnFp8Error("arnfp8_run", st)
+
+
+def arnfp8_run_ex(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps, weight_offset,
+                  scale_ub, rows=None, cols=None, P=None, stream=None, launch=None) -> None:
+    """``arnfp8_run`` with explicit launch options (a ``Launch``, a dict of its
+    fields, or None for automatic)."""
+    rows, cols, P = _shape(inputs, rows, cols, P)
+    if isinstance(launch, dict):
+        launch = Launch(**launch)
+    opt = ctypes.byref(launch) if launch is not None else None
+    st = library().arnfp8_run_ex(_ptr_array(inputs), _ptr(residual_in), _ptr(residual_out),
+                                 _ptr(out_fp8), _ptr(scales), _ptr(gamma), float(eps),
+                                 float(weight_offset), float(scale_ub), rows, cols, P,
+                                 _stream(stream), opt)
+    if st != 0:
+        raise ArnFp8Error("arnfp8_run_ex", st)
 
 
 def arn_sum_bf16(inputs, out, rows=None, cols=None, P=None, stream=None) -> None:

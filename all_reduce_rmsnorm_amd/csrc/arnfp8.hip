@@ -67,7 +67,11 @@ __device__ __forceinline__ u32x2 pack_e4m3(const float v[8]) {
   return (u32x2){(uint32_t)w0, (uint32_t)w1};
 }
 
+// Streaming accesses: every slab, residual and output byte is touched once,
+// so loads and stores are non-temporal (they do not displace gamma in cache).
 __device__ __forceinline__ u32x4 load16(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store16(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store8(u32x2 *p, u32x2 v) { __builtin_nontemporal_store(v, p); }
 
 // Rank-order sum of one chunk: rank 0's value starts the fp32 accumulator,
 // ranks 1..P-1 are added in order, and the total is rounded once to bf16.
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256) void arn_sum_kernel(Slabs in, u32x4 *__restric
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t c = base + u * T;
-      if (c < n16) out[c] = rank_order_sum<P>(x[u]);
+      if (c < n16) store16(out + c, rank_order_sum<P>(x[u]));
     }
   }
 }
@@ -153,15 +157,43 @@ struct RowArgs {
   int c16;  // 16-byte chunks per row
 };
 
+// Loads in flight per lane in the statistics pass: chunks are processed in
+// groups of G whose P slab loads (plus residual and gamma) are all issued
+// before any of them is consumed.
+// The budget is 24 loads (96 VGPRs), less what the fp32 h*g values of the
+// row (8 VGPRs per chunk) leave free under ~200 VGPRs.
+template <int P, int VPT, bool RES_IN>
+constexpr int load_group() {
+  const int budget = (200 - 8 * VPT) / 4 < 24 ? (200 - 8 * VPT) / 4 : 24;
+  int g = 1;
+  while (g * 2 <= VPT && g * 2 * (P + 1 + (RES_IN ? 1 : 0)) <= budget) g *= 2;
+  return g;
+}
+
+// fl32(h * (g + weight_offset)) for the two bf16 elements of one word; the
+// statistics and the quantisation pass both use exactly this expression.
+__device__ __forceinline__ void gain2(uint32_t h, uint32_t g, float woff, float &lo, float &hi) {
+  lo = bf16_lo(h) * (bf16_lo(g) + woff);
+  hi = bf16_hi(h) * (bf16_hi(g) + woff);
+}
+
 // Fused epilogue: workgroups walk the rows grid-stride; lane t owns chunks
-// t + v*T (v < VPT) of the row and keeps h in registers between passes.
+// t + v*T (v < VPT) of the row.  Between the statistics pass and the
+// quantisation pass the row stays in registers: as fp32 h*g for up to 8
+// chunks per lane, as packed bf16 h (gamma re-read from cache) for 16.
+// Chunk indices past the end of a ragged row are clamped to the row's last
+// chunk for the loads (an in-bounds duplicate read), and every store and
+// statistic of such a chunk is masked.
 template <int P, int VPT, bool RES_IN, bool RES_OUT>
 __global__ __launch_bounds__(512) void arnfp8_row_kernel(RowArgs a) {
+  constexpr int G = load_group<P, VPT, RES_IN>();
+  constexpr bool KEEP_HG = VPT <= 8;
   __shared__ float red[2][8][2];  // [row parity][wave][sum h^2, max |h g|]
   const int t = threadIdx.x;
   const int T = blockDim.x;
   const int wave = t >> 6;
   const int nwaves = T >> 6;
+  const int last = a.c16 - 1;
   int parity = 0;
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
@@ -173,33 +205,50 @@ __global__ __launch_bounds__(512) void arnfp8_row_kernel(RowArgs a) {
     const u32x4 *rin = RES_IN ? a.res_in + base : nullptr;
     u32x4 *rout = RES_OUT ? a.res_out + base : nullptr;
     u32x2 *qout = a.out + base;
-    u32x4 h[VPT];
+    float hg[KEEP_HG ? VPT : 1][8];
+    u32x4 hk[KEEP_HG ? 1 : VPT];
     float ss = 0.0f, mx = 0.0f;
 
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const int c = v * T + t;
-      if (c < a.c16) {
-        u32x4 x[P];
+    for (int v0 = 0; v0 < VPT; v0 += G) {
+      u32x4 x[G][P], r[G], g[G];
 #pragma unroll
-        for (int p = 0; p < P; ++p) x[p] = load16(xs[p] + c);
-        u32x4 r;
-        if constexpr (RES_IN) r = load16(rin + c);
-        const u32x4 g = a.gamma[c];
-        u32x4 hv = rank_order_sum<P>(x);
-        if constexpr (RES_IN) hv = add_bf16(hv, r);
-        if constexpr (RES_OUT) rout[c] = hv;
+      for (int k = 0; k < G; ++k) {
+        const int c = min((v0 + k) * T + t, last);
+#pragma unroll
+        for (int p = 0; p < P; ++p) x[k][p] = load16(xs[p] + c);
+        if constexpr (RES_IN) r[k] = load16(rin + c);
+        g[k] = a.gamma[c];
+      }
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int v = v0 + k;
+        const bool valid = v * T + t <= last;
+        u32x4 hv = rank_order_sum<P>(x[k]);
+        if constexpr (RES_IN) hv = add_bf16(hv, r[k]);
+        if constexpr (RES_OUT) {
+          if (valid) store16(rout + v * T + t, hv);
+        }
+        if constexpr (!KEEP_HG) hk[v] = hv;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float h0 = bf16_lo(hv[w]), h1 = bf16_hi(hv[w]);
-          ss += h0 * h0;
-          ss += h1 * h1;
-          const float hg0 = h0 * (bf16_lo(g[w]) + a.woff);
-          const float hg1 = h1 * (bf16_hi(g[w]) + a.woff);
-          mx = fmaxf(mx, fmaxf(fabsf(hg0), fabsf(hg1)));
+          float y0, y1;
+          gain2(hv[w], g[k][w], a.woff, y0, y1);
+          if constexpr (KEEP_HG) {
+            hg[v][2 * w] = y0;
+            hg[v][2 * w + 1] = y1;
+          }
+          if (valid) {
+            const float h0 = bf16_lo(hv[w]), h1 = bf16_hi(hv[w]);
+            ss += h0 * h0;
+            ss += h1 * h1;
+            mx = fmaxf(mx, fmaxf(fabsf(y0), fabsf(y1)));
+          }
         }
-        h[v] = hv;
       }
+      // Keep the next group's loads below this point: hoisting them would
+      // hold more loads in registers than the budget allows.
+      if constexpr (G < VPT) __builtin_amdgcn_sched_barrier(0);
     }
 
     ss = wave_sum(ss);
@@ -221,20 +270,33 @@ __global__ __launch_bounds__(512) void arnfp8_row_kernel(RowArgs a) {
     const float cq = r / scale;
     if (t == 0) a.scales[row] = scale;
 
+    constexpr int QG = KEEP_HG ? 1 : 4;  // gamma re-reads issued together
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      const int c = v * T + t;
-      if (c < a.c16) {
-        const u32x4 g = a.gamma[c];
-        float q[8];
+    for (int v0 = 0; v0 < VPT; v0 += QG) {
+      u32x4 g[QG];
+      if constexpr (!KEEP_HG) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float hg0 = bf16_lo(h[v][w]) * (bf16_lo(g[w]) + a.woff);
-          const float hg1 = bf16_hi(h[v][w]) * (bf16_hi(g[w]) + a.woff);
-          q[2 * w] = fminf(fmaxf(hg0 * cq, -kE4m3Max), kE4m3Max);
-          q[2 * w + 1] = fminf(fmaxf(hg1 * cq, -kE4m3Max), kE4m3Max);
+        for (int k = 0; k < QG; ++k) g[k] = a.gamma[min((v0 + k) * T + t, last)];
+      }
+      if constexpr (!KEEP_HG) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < QG; ++k) {
+        const int v = v0 + k;
+        const int c = v * T + t;
+        float y[8];
+        if constexpr (KEEP_HG) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = hg[v][e];
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) gain2(hk[v][w], g[k][w], a.woff, y[2 * w], y[2 * w + 1]);
         }
-        qout[c] = pack_e4m3(q);
+        if (c <= last) {
+          float q[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = fminf(fmaxf(y[e] * cq, -kE4m3Max), kE4m3Max);
+          store8(qout + c, pack_e4m3(q));
+        }
       }
     }
   }
@@ -360,6 +422,87 @@ RowConfig pick_row_config(int64_t rows, int c16) {
   return cfg;
 }
 
+// Validates the fused call's arguments and fills the kernel arguments.
+int prepare_fused(const void *const *inputs, const void *residual_in, void *residual_out,
+                  void *out_fp8, float *scales, const void *gamma, float eps,
+                  float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
+                  RowArgs *a) {
+  int st = check_inputs(inputs, P);
+  if (st != ARNFP8_OK) return st;
+  if (out_fp8 == nullptr || scales == nullptr || gamma == nullptr) return ARNFP8_NULL_POINTER;
+  if (!aligned(out_fp8, 16) || !aligned(gamma, 16) || !aligned(scales, 4) ||
+      (residual_in && !aligned(residual_in, 16)) || (residual_out && !aligned(residual_out, 16)))
+    return ARNFP8_MISALIGNED;
+
+  // No output may overlap an input or another output; the one exception is
+  // residual_out == residual_in exactly (the in-place residual update).
+  const uintptr_t n = (uintptr_t)(rows * cols);
+  Range ins[ARNFP8_MAX_P + 2];
+  int nin = 0;
+  for (int p = 0; p < P; ++p) ins[nin++] = Range{(uintptr_t)inputs[p], (uintptr_t)inputs[p] + 2 * n};
+  ins[nin++] = Range{(uintptr_t)gamma, (uintptr_t)gamma + 2 * (uintptr_t)cols};
+  const int res_in_slot = residual_in ? nin : -1;
+  if (residual_in) ins[nin++] = Range{(uintptr_t)residual_in, (uintptr_t)residual_in + 2 * n};
+  Range outs[3];
+  int nout = 0;
+  outs[nout++] = Range{(uintptr_t)out_fp8, (uintptr_t)out_fp8 + n};
+  outs[nout++] = Range{(uintptr_t)scales, (uintptr_t)scales + 4 * (uintptr_t)rows};
+  const int res_out_slot = residual_out ? nout : -1;
+  if (residual_out) outs[nout++] = Range{(uintptr_t)residual_out, (uintptr_t)residual_out + 2 * n};
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i) {
+      const bool in_place = o == res_out_slot && i == res_in_slot && residual_out == residual_in;
+      if (!in_place && overlaps(outs[o], ins[i])) return ARNFP8_ALIAS;
+    }
+    for (int o2 = o + 1; o2 < nout; ++o2)
+      if (overlaps(outs[o], outs[o2])) return ARNFP8_ALIAS;
+  }
+
+  for (int p = 0; p < ARNFP8_MAX_P; ++p) a->in.p[p] = (const u32x4 *)inputs[p < P ? p : 0];
+  a->res_in = (const u32x4 *)residual_in;
+  a->res_out = (u32x4 *)residual_out;
+  a->out = (u32x2 *)out_fp8;
+  a->scales = scales;
+  a->gamma = (const u32x4 *)gamma;
+  a->eps = eps;
+  a->woff = weight_offset;
+  a->ub = scale_ub;
+  a->cols_f = (float)cols;
+  a->rows = rows;
+  a->c16 = (int)(cols / 8);
+  return ARNFP8_OK;
+}
+
+// Resolves the launch options against the automatic choice.
+int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfig *cfg) {
+  *cfg = pick_row_config(rows, c16);
+  if (opt == nullptr) return ARNFP8_OK;
+  if (opt->variant != ARNFP8_VARIANT_AUTO && opt->variant != ARNFP8_VARIANT_ROW)
+    return ARNFP8_BAD_CONFIG;
+  if (opt->threads < 0 || opt->vpt < 0 || opt->grid < 0) return ARNFP8_BAD_CONFIG;
+  if (opt->threads) {
+    if (opt->threads % 64 != 0 || opt->threads > 512) return ARNFP8_BAD_CONFIG;
+    cfg->threads = opt->threads;
+    if (!opt->vpt) {  // the smallest chunks-per-lane that covers the row
+      static const int vpts[5] = {1, 2, 4, 8, 16};
+      cfg->vpt = 0;
+      for (int i = 0; i < 5 && !cfg->vpt; ++i)
+        if ((int64_t)vpts[i] * cfg->threads >= c16) cfg->vpt = vpts[i];
+      if (!cfg->vpt) return ARNFP8_BAD_CONFIG;
+    }
+  }
+  if (opt->vpt) {
+    if (opt->vpt != 1 && opt->vpt != 2 && opt->vpt != 4 && opt->vpt != 8 && opt->vpt != 16)
+      return ARNFP8_BAD_CONFIG;
+    cfg->vpt = opt->vpt;
+    if (!opt->threads) cfg->threads = ((c16 + cfg->vpt - 1) / cfg->vpt + 63) / 64 * 64;
+    if (cfg->threads > 512) return ARNFP8_BAD_CONFIG;
+  }
+  if ((int64_t)cfg->threads * cfg->vpt < c16) return ARNFP8_BAD_CONFIG;
+  if (opt->grid) cfg->grid = opt->grid;
+  return ARNFP8_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ C ABI --
@@ -391,59 +534,31 @@ extern "C" int arn_sum_bf16(const void *const *inputs, void *out, int64_t rows, 
   return launch_status();
 }
 
+extern "C" int arnfp8_run_ex(const void *const *inputs, const void *residual_in,
+                             void *residual_out, void *out_fp8, float *scales, const void *gamma,
+                             float eps, float weight_offset, float scale_ub, int64_t rows,
+                             int64_t cols, int P, hipStream_t stream, const arnfp8_launch *opt) {
+  int st = check_shape(rows, cols, P);
+  if (st != ARNFP8_OK) return st;
+  RowConfig cfg;
+  st = resolve_row_config(opt, rows, (int)(cols / 8), &cfg);
+  if (st != ARNFP8_OK) return st;
+  if (rows == 0) return ARNFP8_OK;
+  RowArgs a;
+  st = prepare_fused(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                     weight_offset, scale_ub, rows, cols, P, &a);
+  if (st != ARNFP8_OK) return st;
+  hipLaunchKernelGGL(row_table(P, cfg.vpt, residual_in != nullptr, residual_out != nullptr),
+                     dim3(cfg.grid), dim3(cfg.threads), 0, stream, a);
+  return launch_status();
+}
+
 extern "C" int arnfp8_run(const void *const *inputs, const void *residual_in, void *residual_out,
                           void *out_fp8, float *scales, const void *gamma, float eps,
                           float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
                           hipStream_t stream) {
-  int st = check_shape(rows, cols, P);
-  if (st != ARNFP8_OK) return st;
-  if (rows == 0) return ARNFP8_OK;
-  st = check_inputs(inputs, P);
-  if (st != ARNFP8_OK) return st;
-  if (out_fp8 == nullptr || scales == nullptr || gamma == nullptr) return ARNFP8_NULL_POINTER;
-  if (!aligned(out_fp8, 16) || !aligned(gamma, 16) || !aligned(scales, 4) ||
-      (residual_in && !aligned(residual_in, 16)) || (residual_out && !aligned(residual_out, 16)))
-    return ARNFP8_MISALIGNED;
-
-  const uintptr_t n = (uintptr_t)(rows * cols);
-  Range ins[ARNFP8_MAX_P + 2];
-  int nin = 0;
-  for (int p = 0; p < P; ++p) ins[nin++] = Range{(uintptr_t)inputs[p], (uintptr_t)inputs[p] + 2 * n};
-  ins[nin++] = Range{(uintptr_t)gamma, (uintptr_t)gamma + 2 * (uintptr_t)cols};
-  const Range res_in_r{(uintptr_t)residual_in, (uintptr_t)residual_in + 2 * n};
-  if (residual_in) ins[nin++] = res_in_r;
-  Range outs[3];
-  int nout = 0;
-  outs[nout++] = Range{(uintptr_t)out_fp8, (uintptr_t)out_fp8 + n};
-  outs[nout++] = Range{(uintptr_t)scales, (uintptr_t)scales + 4 * (uintptr_t)rows};
-  if (residual_out) outs[nout++] = Range{(uintptr_t)residual_out, (uintptr_t)residual_out + 2 * n};
-  for (int o = 0; o < nout; ++o) {
-    for (int i = 0; i < nin; ++i) {
-      const bool in_place = residual_out && residual_out == residual_in && o == 2 &&
-                            ins[i].lo == res_in_r.lo && ins[i].hi == res_in_r.hi;
-      if (!in_place && overlaps(outs[o], ins[i])) return ARNFP8_ALIAS;
-    }
-    for (int o2 = o + 1; o2 < nout; ++o2)
-      if (overlaps(outs[o], outs[o2])) return ARNFP8_ALIAS;
-  }
-
-  RowArgs a;
-  for (int p = 0; p < ARNFP8_MAX_P; ++p) a.in.p[p] = (const u32x4 *)inputs[p < P ? p : 0];
-  a.res_in = (const u32x4 *)residual_in;
-  a.res_out = (u32x4 *)residual_out;
-  a.out = (u32x2 *)out_fp8;
-  a.scales = scales;
-  a.gamma = (const u32x4 *)gamma;
-  a.eps = eps;
-  a.woff = weight_offset;
-  a.ub = scale_ub;
-  a.cols_f = (float)cols;
-  a.rows = rows;
-  a.c16 = (int)(cols / 8);
-  const RowConfig cfg = pick_row_config(rows, a.c16);
-  hipLaunchKernelGGL(row_table(P, cfg.vpt, residual_in != nullptr, residual_out != nullptr),
-                     dim3(cfg.grid), dim3(cfg.threads), 0, stream, a);
-  return launch_status();
+  return arnfp8_run_ex(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                       weight_offset, scale_ub, rows, cols, P, stream, nullptr);
 }
 
 extern "C" const char *arnfp8_status_string(int status) {

@@ -37,7 +37,9 @@
  *     state; a call that returns an error has launched nothing.
  *   - Execution is asynchronous on `stream` (NULL = the default stream);
  *     results are visible to later work on that stream.  Results are
- *     deterministic: bitwise identical on every call and every launch shape.
+ *     deterministic: bitwise identical on every call with the same arguments
+ *     (the automatic launch shape depends only on rows, cols, P and the
+ *     device), including calls replayed from a captured graph.
  *   - Concurrent calls on different streams must not share output buffers.
  *   - Non-finite inputs are not supported (the results are unspecified).
  */
@@ -93,6 +95,32 @@ int arnfp8_run(const void *const *inputs, const void *residual_in, void *residua
                void *out_fp8, float *scales, const void *gamma, float eps,
                float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
                hipStream_t stream);
+
+/* Kernel variants selectable through arnfp8_launch.variant. */
+#define ARNFP8_VARIANT_AUTO 0 /* the library's choice from (rows, cols, P)        */
+#define ARNFP8_VARIANT_ROW 1  /* one workgroup per row, rows walked grid-stride  */
+
+/* Launch options for arnfp8_run_ex.  Zero in any field means "automatic". */
+typedef struct arnfp8_launch {
+  int variant; /* ARNFP8_VARIANT_*                                               */
+  int threads; /* lanes per workgroup: a multiple of 64 in [64, 512]           */
+  int vpt;     /* 16-byte chunks per lane: 1, 2, 4, 8 or 16                    */
+  int grid;    /* workgroups; rows are walked grid-stride (>= 1)               */
+} arnfp8_launch;
+
+/*
+ * arnfp8_run_ex -- arnfp8_run with explicit launch options (for tuning and for
+ * testing every kernel shape).  `opt` may be NULL (= arnfp8_run).  The options
+ * must satisfy threads * vpt * 8 >= cols; otherwise, or for an out-of-range
+ * field, the call returns ARNFP8_BAD_CONFIG without launching.  bf16 outputs
+ * do not depend on the options; fp32 scales and fp8 codes may differ in the
+ * last bits between launch shapes (the sum of squares is reduced in a
+ * shape-dependent order), each staying within the operation's tolerance.
+ */
+int arnfp8_run_ex(const void *const *inputs, const void *residual_in, void *residual_out,
+                  void *out_fp8, float *scales, const void *gamma, float eps,
+                  float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
+                  hipStream_t stream, const arnfp8_launch *opt);
 
 /*
  * arn_sum_bf16 -- the reduction alone: out = s as defined for arnfp8_run.
