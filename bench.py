@@ -81,24 +81,22 @@ def step_fn(w, d, arn):
 
 
 def time_steps(torch, fn, steps, warmup):
-    """Wall time of exactly `steps` calls (synchronised on both sides) and the
-    average per-launch duration from HIP events on the launch stream."""
+    """Exactly `steps` calls, synchronised on both sides: (wall ms per step,
+    ms per launch from one HIP event pair on the launch stream around the
+    same `steps` launches, which run back to back)."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(steps):
         fn()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-    return wall / steps * 1e3, kern_ms
+    return wall / steps * 1e3, a.elapsed_time(b) / steps
 
 
 def graph_us_per_call(torch, fn, calls=100, reps=5):
@@ -389,6 +387,32 @@ def main():
                      "traffic": traffic, "kernel_us": round(kern_ms * 1e3, 3),
                      "kernel_source_hash": khash},
     }
+    if not w.sum_only and not args.no_latency:
+        # The unfused chain the fusion removes: the sum is written to HBM as
+        # bf16 and read back by a second launch (the fused kernel with P = 1).
+        s_buf = d["sum_out"]
+        unfused = lambda: (arn.arn_sum_bf16(d["inputs"], s_buf),
+                           arn.arnfp8_run([s_buf], d["residual"], d["res_out"], d["out"],
+                                          d["scales"], d["gamma"], w.eps, w.weight_offset,
+                                          w.scale_ub))
+        un_ms, _ = time_steps(torch, unfused, max(5, args.steps // 2), 3)
+        result["unfused_two_launch"] = {
+            "us_per_call": round(un_ms * 1e3, 2),
+            "extra_bytes_per_step": 4 * w.numel,
+            "fused_speedup": round(un_ms / ms_per_step, 3),
+        }
+        log(f"bench: unfused two-launch chain {un_ms * 1e3:.2f} us/step")
+        # Achievable-bandwidth references on the same device: a plain copy
+        # (the P = 1 sum kernel, 1 GiB each way) and the P-slab sum alone.
+        src = torch.ones((65536, 8192), dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        cp_ms, cp_k = time_steps(torch, lambda: arn.arn_sum_bf16([src], dst), 10, 3)
+        del src, dst
+        sm_ms, sm_k = time_steps(torch, lambda: arn.arn_sum_bf16(d["inputs"], s_buf), 10, 3)
+        result["reference_kernels"] = {
+            "copy_1GiB_gbs": round(2 * (1 << 30) / (cp_k * 1e-3) / 1e9, 1),
+            "sum_only_same_slabs_gbs": round((2 * w.P + 2) * w.numel / (sm_k * 1e-3) / 1e9, 1),
+        }
     if not args.no_latency:
         lat = {}
         for name in DECODE_WORKLOADS:

@@ -323,3 +323,49 @@ def test_errors_raise_before_launch(arn):
         arn.arnfp8_run([x[:, 4:]], None, None, out, s, g, 1e-6, 0.0, 1.0, rows=4, cols=56)
     assert e.value.status == 2
     torch.cuda.synchronize()
+
+
+def test_unfused_two_launch_chain_is_bitwise_equal(arn, synth):
+    """arn_sum_bf16 to HBM, then the fused kernel with P = 1 on the sum: the
+    same bytes as the single fused launch (the fusion changes no result)."""
+    w = synth.WORKLOADS["unit_offset_p8_128x8192"]
+    d = synth.make_inputs(w, device=DEV)
+    fused = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                      residual=d["residual"], in_place=False)
+    s = torch.empty_like(d["inputs"][0])
+    arn.arn_sum_bf16(d["inputs"], s)
+    unfused = run_fused(arn, [s], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                        residual=d["residual"], in_place=False)
+    assert torch.equal(fused[0].view(torch.uint8), unfused[0].view(torch.uint8))
+    assert torch.equal(fused[1], unfused[1]) and torch.equal(fused[2], unfused[2])
+
+
+@pytest.mark.parametrize("launch", [dict(threads=64, vpt=16), dict(threads=128, vpt=8),
+                                    dict(threads=256, vpt=4), dict(threads=512, vpt=2),
+                                    dict(threads=448, vpt=4, grid=7), dict(threads=320, vpt=4, grid=1)])
+def test_every_launch_shape_matches_the_oracle(arn, orc, launch):
+    rows, cols = 13, 7176  # 897 chunks: ragged for every shape above
+    print(f"[fused] launch {launch}", flush=True)
+    g = torch.Generator().manual_seed(sum(launch.values()))
+    xs = [(torch.randn((rows, cols), generator=g) * 0.5).to(torch.bfloat16) for _ in range(8)]
+    res = torch.randn((rows, cols), generator=g).to(torch.bfloat16)
+    gamma = (torch.rand((cols,), generator=g) * 0.4 + 0.8).to(torch.bfloat16)
+    out = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=DEV)
+    scales = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    res_out = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    arn.arnfp8_run_ex([x.to(DEV) for x in xs], res.to(DEV), res_out, out, scales, gamma.to(DEV),
+                      1e-6, 0.0, 1200.0, launch=launch)
+    torch.cuda.synchronize()
+    check_against_oracle(orc, xs, gamma, 1e-6, 0.0, 1200.0, res, out, scales, res_out)
+
+
+def test_bad_launch_options_rejected(arn):
+    x = torch.zeros((4, 1024), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((4, 1024), dtype=torch.float8_e4m3fn, device=DEV)
+    s = torch.empty((4,), dtype=torch.float32, device=DEV)
+    g = torch.ones((1024,), dtype=torch.bfloat16, device=DEV)
+    for bad in (dict(threads=96), dict(threads=1024), dict(vpt=3), dict(threads=64, vpt=1),
+                dict(grid=-1), dict(variant=9)):
+        with pytest.raises(arn.ArnFp8Error) as e:
+            arn.arnfp8_run_ex([x], None, None, out, s, g, 1e-6, 0.0, 1.0, launch=bad)
+        assert e.value.status == 7, bad
