@@ -16,7 +16,8 @@ import os
 __all__ = [
     "ArnFp8Error", "MAX_P", "MAX_COLS", "STATUS",
     "arnfp8_run", "arnfp8_run_ex", "arn_sum_bf16", "arnfp8_status_string", "Launch",
-    "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW",
+    "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW", "arnfp8_stage_bytes",
+    "arnfp8_run_share", "SIMD_WIDTH",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,9 @@ MAX_COLS = 65536
 STATUS = {
     0: "ARNFP8_OK", 1: "ARNFP8_NULL_POINTER", 2: "ARNFP8_MISALIGNED", 3: "ARNFP8_BAD_SHAPE",
     4: "ARNFP8_BAD_P", 5: "ARNFP8_ALIAS", 6: "ARNFP8_HIP_ERROR", 7: "ARNFP8_BAD_CONFIG",
+    8: "ARNFP8_BAD_SHARE",
 }
+SIMD_WIDTH = 16
 
 
 class ArnFp8Error(RuntimeError):
@@ -73,6 +76,12 @@ def library() -> ctypes.CDLL:
         L.arnfp8_run_ex.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
                                     ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int, vp,
                                     ctypes.POINTER(Launch)]
+        L.arnfp8_stage_bytes.restype = ctypes.c_int64
+        L.arnfp8_stage_bytes.argtypes = [i64, i64, ctypes.c_int]
+        L.arnfp8_run_share.restype = ctypes.c_int
+        L.arnfp8_run_share.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, vp]
         L.arn_sum_bf16.restype = ctypes.c_int
         L.arn_sum_bf16.argtypes = [ctypes.POINTER(vp), vp, i64, i64, ctypes.c_int, vp]
         L.arnfp8_status_string.restype = ctypes.c_char_p
@@ -162,3 +171,20 @@ def arn_sum_bf16(inputs, out, rows=None, cols=None, P=None, stream=None) -> None
     st = library().arn_sum_bf16(_ptr_array(inputs), _ptr(out), rows, cols, P, _stream(stream))
     if st != 0:
         raise ArnFp8Error("arn_sum_bf16", st)
+
+
+def arnfp8_stage_bytes(rows: int, cols: int, ngpus: int) -> int:
+    """Bytes of one rank's staging slot in the two-stage layout (-1 if invalid)."""
+    return int(library().arnfp8_stage_bytes(int(rows), int(cols), int(ngpus)))
+
+
+def arnfp8_run_share(inputs, residual_in, residual_out, staging, gamma, eps, weight_offset,
+                     scale_ub, rows=None, cols=None, P=None, ngpus=1, rank=0, stream=None) -> None:
+    """The fused epilogue on rank ``rank``'s row share, fp8 rows + scales into ``staging``."""
+    rows, cols, P = _shape(inputs, rows, cols, P)
+    st = library().arnfp8_run_share(_ptr_array(inputs), _ptr(residual_in), _ptr(residual_out),
+                                    _ptr(staging), _ptr(gamma), float(eps), float(weight_offset),
+                                    float(scale_ub), rows, cols, P, int(ngpus), int(rank),
+                                    _stream(stream))
+    if st != 0:
+        raise ArnFp8Error("arnfp8_run_share", st)

@@ -561,6 +561,71 @@ extern "C" int arnfp8_run(const void *const *inputs, const void *residual_in, vo
                        weight_offset, scale_ub, rows, cols, P, stream, nullptr);
 }
 
+extern "C" int64_t arnfp8_stage_bytes(int64_t rows, int64_t cols, int ngpus) {
+  if (rows < 0 || cols <= 0 || ngpus < 1) return -1;
+  const int64_t S = (rows + ngpus - 1) / ngpus;
+  if (S > 0 && cols > (INT64_MAX / 2) / S) return -1;
+  const int64_t scale_bytes = S * (int64_t)sizeof(float);
+  return S * cols + (scale_bytes + ARNFP8_SIMD_WIDTH - 1) / ARNFP8_SIMD_WIDTH * ARNFP8_SIMD_WIDTH;
+}
+
+extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_in,
+                                void *residual_out, void *staging, const void *gamma, float eps,
+                                float weight_offset, float scale_ub, int64_t rows, int64_t cols,
+                                int P, int ngpus, int rank, hipStream_t stream) {
+  int st = check_shape(rows, cols, P);
+  if (st != ARNFP8_OK) return st;
+  if (ngpus < 1 || rank < 0 || rank >= ngpus) return ARNFP8_BAD_SHARE;
+  if (rows == 0) return ARNFP8_OK;
+  st = check_inputs(inputs, P);
+  if (st != ARNFP8_OK) return st;
+  if (staging == nullptr) return ARNFP8_NULL_POINTER;
+  if (!aligned(staging, 16)) return ARNFP8_MISALIGNED;
+
+  const int64_t S = (rows + ngpus - 1) / ngpus;
+  const int64_t first = (int64_t)rank * S < rows ? (int64_t)rank * S : rows;
+  const int64_t count = (first + S < rows ? first + S : rows) - first;
+  // The share's rows of every full-size tensor (bf16: 2 bytes per element).
+  const uintptr_t skip = (uintptr_t)(first * cols * 2);
+  const void *shifted[ARNFP8_MAX_P];
+  for (int p = 0; p < P; ++p) shifted[p] = (const char *)inputs[p] + skip;
+  const void *rin = residual_in ? (const char *)residual_in + skip : nullptr;
+  void *rout = residual_out ? (char *)residual_out + skip : nullptr;
+  uint8_t *out = (uint8_t *)staging;
+  float *scales = (float *)(out + S * cols);
+
+  if (gamma == nullptr) return ARNFP8_NULL_POINTER;
+  // The whole slot must stay clear of every full-size input and output.
+  const Range slot{(uintptr_t)staging,
+                   (uintptr_t)staging + (uintptr_t)arnfp8_stage_bytes(rows, cols, ngpus)};
+  const uintptr_t full = (uintptr_t)(rows * cols * 2);
+  for (int p = 0; p < P; ++p)
+    if (overlaps(slot, Range{(uintptr_t)inputs[p], (uintptr_t)inputs[p] + full})) return ARNFP8_ALIAS;
+  if (residual_in && overlaps(slot, Range{(uintptr_t)residual_in, (uintptr_t)residual_in + full}))
+    return ARNFP8_ALIAS;
+  if (residual_out && overlaps(slot, Range{(uintptr_t)residual_out, (uintptr_t)residual_out + full}))
+    return ARNFP8_ALIAS;
+  if (overlaps(slot, Range{(uintptr_t)gamma, (uintptr_t)gamma + 2 * (uintptr_t)cols}))
+    return ARNFP8_ALIAS;
+  if (count == 0) {
+    if (!aligned(gamma, 16) || (residual_in && !aligned(residual_in, 16)) ||
+        (residual_out && !aligned(residual_out, 16)))
+      return ARNFP8_MISALIGNED;
+    return ARNFP8_OK;
+  }
+
+  RowConfig cfg;
+  st = resolve_row_config(nullptr, count, (int)(cols / 8), &cfg);
+  if (st != ARNFP8_OK) return st;
+  RowArgs a;
+  st = prepare_fused(shifted, rin, rout, out, scales, gamma, eps, weight_offset, scale_ub, count,
+                     cols, P, &a);
+  if (st != ARNFP8_OK) return st;
+  hipLaunchKernelGGL(row_table(P, cfg.vpt, residual_in != nullptr, residual_out != nullptr),
+                     dim3(cfg.grid), dim3(cfg.threads), 0, stream, a);
+  return launch_status();
+}
+
 extern "C" const char *arnfp8_status_string(int status) {
   switch (status) {
     case ARNFP8_OK: return "ok";
@@ -571,6 +636,7 @@ extern "C" const char *arnfp8_status_string(int status) {
     case ARNFP8_ALIAS: return "an output overlaps an input or another output";
     case ARNFP8_HIP_ERROR: return "HIP launch error";
     case ARNFP8_BAD_CONFIG: return "invalid launch configuration";
+    case ARNFP8_BAD_SHARE: return "bad share: ngpus must be >= 1 and 0 <= rank < ngpus";
     default: return "unknown status";
   }
 }

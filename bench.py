@@ -402,6 +402,22 @@ def main():
             "fused_speedup": round(un_ms / ms_per_step, 3),
         }
         log(f"bench: unfused two-launch chain {un_ms * 1e3:.2f} us/step")
+        # One rank's share of the two-stage layout (8 ranks): the single-GPU
+        # half of the large-payload path, at its real shape.
+        ngpus = 8
+        stg = torch.empty((arn.arnfp8_stage_bytes(w.rows, w.cols, ngpus),), dtype=torch.uint8,
+                          device=dev)
+        share_rows = -(-w.rows // ngpus)
+        sh_ms, sh_k = time_steps(torch, lambda: arn.arnfp8_run_share(
+            d["inputs"], d["residual"], d["res_out"], stg, d["gamma"], w.eps, w.weight_offset,
+            w.scale_ub, ngpus=ngpus, rank=3), max(10, args.steps), 3)
+        share_bytes = (2 * w.P + 4 + 1) * share_rows * w.cols + 4 * share_rows + 2 * w.cols
+        result["two_stage_share"] = {
+            "ngpus": ngpus, "rank": 3, "rows": share_rows,
+            "us_per_call": round(sh_k * 1e3, 2),
+            "gbs": round(share_bytes / (sh_k * 1e-3) / 1e9, 1),
+        }
+        del stg
         # Achievable-bandwidth references on the same device: a plain copy
         # (the P = 1 sum kernel, 1 GiB each way) and the P-slab sum alone.
         src = torch.ones((65536, 8192), dtype=torch.bfloat16, device=dev)

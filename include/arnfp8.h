@@ -67,6 +67,7 @@ extern "C" {
                                  (residual_out == residual_in is allowed)      */
 #define ARNFP8_HIP_ERROR 6    /* the launch failed (hipGetLastError)             */
 #define ARNFP8_BAD_CONFIG 7   /* an arnfp8_run_ex launch option is invalid       */
+#define ARNFP8_BAD_SHARE 8    /* ngpus < 1, or rank outside [0, ngpus)           */
 
 /*
  * arnfp8_run -- the fused epilogue.  For every row i and column j:
@@ -129,6 +130,40 @@ int arnfp8_run_ex(const void *const *inputs, const void *residual_in, void *resi
  */
 int arn_sum_bf16(const void *const *inputs, void *out, int64_t rows, int64_t cols, int P,
                  hipStream_t stream);
+
+/*
+ * Two-stage (large payload) row share.  With `ngpus` ranks each rank owns
+ * S = ceil(rows / ngpus) consecutive rows, rank k the rows [k*S, min(rows,
+ * (k+1)*S)) (possibly none).  It reduces and normalises only its share and
+ * writes the share's fp8 rows and scales into one staging slot, from which the
+ * other ranks gather it:
+ *   bytes [0, S*cols)                        fp8 e4m3fn rows of the share
+ *   bytes [S*cols, S*cols + S*4)             fp32 scales of the share
+ *   padded to ARNFP8_SIMD_WIDTH              (slot size: arnfp8_stage_bytes)
+ * Source: Modular Mojo API docs, "allreduce_rmsnorm_fp8" (2-stage path:
+ * signal buffer sizing of ceildiv(rows, ngpus) * cols fp8 bytes plus the
+ * scales aligned up to the SIMD width; the signal header is not part of the
+ * slot here).  Rows past the share's end in a shorter last share leave their
+ * slot bytes untouched.
+ */
+#define ARNFP8_SIMD_WIDTH 16
+
+/* Bytes of one staging slot, or -1 for rows < 0, cols <= 0, ngpus < 1. */
+int64_t arnfp8_stage_bytes(int64_t rows, int64_t cols, int ngpus);
+
+/*
+ * arnfp8_run_share -- arnfp8_run restricted to rank `rank`'s share.
+ * inputs, residual_in, residual_out are the full [rows, cols] tensors; only
+ * the share's rows are read, and only the share's rows of residual_out are
+ * written.  staging is device memory of arnfp8_stage_bytes(rows, cols, ngpus)
+ * bytes, 16-byte aligned, overlapping no input or residual_out.  Every other
+ * argument and rule is that of arnfp8_run.  An empty share returns ARNFP8_OK
+ * after validation and launches nothing.
+ */
+int arnfp8_run_share(const void *const *inputs, const void *residual_in, void *residual_out,
+                     void *staging, const void *gamma, float eps, float weight_offset,
+                     float scale_ub, int64_t rows, int64_t cols, int P, int ngpus, int rank,
+                     hipStream_t stream);
 
 /* Human-readable text for a status code (a static string; never NULL). */
 const char *arnfp8_status_string(int status);

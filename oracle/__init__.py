@@ -68,6 +68,15 @@ def lib() -> ctypes.CDLL:
         L.oracle_arnfp8.argtypes = [ctypes.POINTER(_u16p), ctypes.c_int, _u16p, _u16p,
                                     _u8p, _f32p, _u16p, ctypes.c_float, ctypes.c_float,
                                     ctypes.c_float, ctypes.c_int64, ctypes.c_int64]
+        L.oracle_share_rows.restype = None
+        L.oracle_share_rows.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int64),
+                                        ctypes.POINTER(ctypes.c_int64)]
+        L.oracle_stage_bytes.restype = ctypes.c_int64
+        L.oracle_stage_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+        L.oracle_stage_share.restype = ctypes.c_int
+        L.oracle_stage_share.argtypes = [_u8p, _f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, _u8p]
         _lib = L
     return _lib
 
@@ -157,3 +166,34 @@ def arnfp8(inputs, gamma, eps, weight_offset, scale_ub, residual_in=None,
     if st != 0:
         raise ValueError(f"oracle_arnfp8 failed with status {st}")
     return out, scales, res_out
+
+
+# ------------------------------------------------ two-stage row share ----
+
+SIMD_WIDTH = 16  # bytes: the scales of a staging slot are padded to this
+
+
+def share_rows(rows: int, ngpus: int, rank: int):
+    """(first row, row count) of rank ``rank``'s share."""
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    lib().oracle_share_rows(int(rows), int(ngpus), int(rank), ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
+def stage_bytes(rows: int, cols: int, ngpus: int, simd_width: int = SIMD_WIDTH) -> int:
+    return lib().oracle_stage_bytes(int(rows), int(cols), int(ngpus), int(simd_width))
+
+
+def stage_share(out_fp8, scales, ngpus: int, rank: int, simd_width: int = SIMD_WIDTH,
+                fill: int = 0) -> np.ndarray:
+    """Rank ``rank``'s staging slot built from a full fused output; bytes the
+    share does not fill hold ``fill``."""
+    out_fp8 = np.ascontiguousarray(out_fp8, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32).reshape(-1)
+    rows, cols = out_fp8.shape
+    slot = np.full((stage_bytes(rows, cols, ngpus, simd_width),), fill, dtype=np.uint8)
+    st = lib().oracle_stage_share(_ptr(out_fp8, _u8p), _ptr(scales, _f32p), rows, cols, ngpus,
+                                  rank, simd_width, _ptr(slot, _u8p))
+    if st != 0:
+        raise ValueError(f"oracle_stage_share failed with status {st}")
+    return slot

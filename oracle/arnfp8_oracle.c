@@ -277,3 +277,50 @@ int oracle_arnfp8(const uint16_t *const *inputs, int P,
     free(y);
     return ORACLE_OK;
 }
+
+/* ------------------------------------------- two-stage share and staging -- */
+/*
+ * The layout of one rank's slot follows the signal-buffer sizing of the
+ * 2-stage path: ceildiv(rows, ngpus) * cols bytes of fp8 data, then the
+ * share's scales, ceildiv(rows, ngpus) * sizeof(float) bytes aligned up to
+ * the SIMD width (Modular Mojo API docs, "allreduce_rmsnorm_fp8", the note
+ * on signal buffer sizing; the signal header itself is not part of the slot).
+ */
+
+void oracle_share_rows(int64_t rows, int ngpus, int rank, int64_t *first, int64_t *count)
+{
+    int64_t S = (rows + ngpus - 1) / ngpus;
+    int64_t lo = (int64_t)rank * S;
+    int64_t hi = lo + S;
+    if (lo > rows)
+        lo = rows;
+    if (hi > rows)
+        hi = rows;
+    *first = lo;
+    *count = hi - lo;
+}
+
+int64_t oracle_stage_bytes(int64_t rows, int64_t cols, int ngpus, int simd_width)
+{
+    int64_t S = (rows + ngpus - 1) / ngpus;
+    int64_t scale_bytes = S * (int64_t)sizeof(float);
+    int64_t padded = (scale_bytes + simd_width - 1) / simd_width * simd_width;
+    return S * cols + padded;
+}
+
+int oracle_stage_share(const uint8_t *out_fp8, const float *scales, int64_t rows,
+                       int64_t cols, int ngpus, int rank, int simd_width, uint8_t *staging)
+{
+    if (out_fp8 == NULL || scales == NULL || staging == NULL || ngpus < 1 || rank < 0 ||
+        rank >= ngpus || rows < 0 || cols <= 0 || simd_width < 1)
+        return ORACLE_BAD_ARG;
+    int64_t S = (rows + ngpus - 1) / ngpus;
+    int64_t first, count;
+    oracle_share_rows(rows, ngpus, rank, &first, &count);
+    for (int64_t i = 0; i < count; ++i) {
+        for (int64_t j = 0; j < cols; ++j)
+            staging[i * cols + j] = out_fp8[(first + i) * cols + j];
+        memcpy(staging + S * cols + i * (int64_t)sizeof(float), &scales[first + i], sizeof(float));
+    }
+    return ORACLE_OK;
+}

@@ -74,6 +74,27 @@ int oracle_arnfp8(const uint16_t *const *inputs, int P,
                   float eps, float weight_offset, float scale_ub,
                   int64_t rows, int64_t cols);
 
+/* ---- two-stage row share and its staging layout ------------------------ */
+/*
+ * In the two-stage (large payload) path each of `ngpus` ranks owns
+ * S = ceil(rows / ngpus) consecutive rows: rank k owns [k*S, min(rows, (k+1)*S)).
+ * It writes the fp8 rows of its share, then their fp32 scales, into one
+ * staging slot:  S * cols bytes of fp8 data, then S * 4 bytes of scales
+ * padded up to a multiple of `simd_width` bytes.
+ */
+
+/* First row and row count of rank `rank`'s share (count may be 0). */
+void oracle_share_rows(int64_t rows, int ngpus, int rank, int64_t *first, int64_t *count);
+
+/* Bytes of one staging slot (fp8 data + padded scales). */
+int64_t oracle_stage_bytes(int64_t rows, int64_t cols, int ngpus, int simd_width);
+
+/* Place rank `rank`'s share of a full fused output (out_fp8 [rows, cols],
+ * scales [rows]) into `staging` (oracle_stage_bytes bytes; bytes of the slot
+ * that the share does not fill are left untouched). */
+int oracle_stage_share(const uint8_t *out_fp8, const float *scales, int64_t rows,
+                       int64_t cols, int ngpus, int rank, int simd_width, uint8_t *staging);
+
 #ifdef __cplusplus
 }
 #endif

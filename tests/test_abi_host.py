@@ -167,3 +167,35 @@ def test_product_package_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in re.sub(r"#.*|//.*", "", text).lower() or f == "synth.py", f
+
+
+def test_stage_bytes_agrees_with_the_oracle(L):
+    import oracle
+
+    for rows in (0, 1, 5, 33, 1000, 8192):
+        for cols in (8, 24, 2880, 7168):
+            for ngpus in (1, 2, 3, 4, 8):
+                assert L.arnfp8_stage_bytes(rows, cols, ngpus) == oracle.stage_bytes(rows, cols, ngpus)
+    assert L.arnfp8_stage_bytes(-1, 8, 1) == -1
+    assert L.arnfp8_stage_bytes(4, 0, 1) == -1
+    assert L.arnfp8_stage_bytes(4, 8, 0) == -1
+
+
+def test_share_validation_codes(L):
+    x0, x1 = BASE, BASE + 10 * MB
+    stg, g = BASE + 100 * MB, BASE + 300 * MB
+
+    def share(ngpus, rank, staging=stg, rows=16, cols=256, inputs=(x0, x1), gamma=g):
+        return L.arnfp8_run_share(_arr(*inputs), None, None, staging, gamma, 1e-6, 0.0, 1.0,
+                                  rows, cols, len(inputs), ngpus, rank, None)
+
+    assert share(0, 0) == 8
+    assert share(4, 4) == 8
+    assert share(4, -1) == 8
+    assert share(4, 1, staging=None) == NULLP
+    assert share(4, 1, staging=stg + 8) == MISALIGNED
+    assert share(4, 1, staging=x1 + 512) == ALIAS
+    assert share(4, 1, gamma=None) == NULLP
+    assert share(4, 1, cols=12) == BAD_SHAPE
+    # an empty share validates and returns OK without launching
+    assert share(8, 7, rows=5) == OK

@@ -369,3 +369,51 @@ def test_bad_launch_options_rejected(arn):
         with pytest.raises(arn.ArnFp8Error) as e:
             arn.arnfp8_run_ex([x], None, None, out, s, g, 1e-6, 0.0, 1.0, launch=bad)
         assert e.value.status == 7, bad
+
+
+@pytest.mark.parametrize("ngpus", [1, 3, 8])
+def test_two_stage_share_and_staging_layout(arn, orc, ngpus):
+    """Every rank's share: the staging slot holds the oracle's fp8 rows and
+    scales of that share; the share's residual rows are updated, no other row
+    is touched; all shares together equal the single full call bitwise."""
+    import oracle as orc_mod
+
+    rows, cols, P = 37, 2880, 4
+    print(f"[share] ngpus={ngpus}", flush=True)
+    g = torch.Generator().manual_seed(ngpus)
+    xs = [(torch.randn((rows, cols), generator=g) * 0.5).to(torch.bfloat16) for _ in range(P)]
+    res = torch.randn((rows, cols), generator=g).to(torch.bfloat16)
+    gamma = (torch.rand((cols,), generator=g) * 0.4 + 0.8).to(torch.bfloat16)
+    q_ref, s_ref, h_ref = orc.arnfp8([_bits(x) for x in xs], _bits(gamma), 1e-6, 0.0, 1200.0,
+                                     residual_in=_bits(res))
+    dxs = [x.to(DEV) for x in xs]
+    full = run_fused(arn, dxs, gamma.to(DEV), 1e-6, 0.0, 1200.0, residual=res.to(DEV),
+                     in_place=False)
+    nbytes = arn.arnfp8_stage_bytes(rows, cols, ngpus)
+    assert nbytes == orc_mod.stage_bytes(rows, cols, ngpus)
+    S = -(-rows // ngpus)
+    for rank in range(ngpus):
+        staging = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+        res_out = torch.full((rows, cols), 7.0, dtype=torch.bfloat16, device=DEV)
+        arn.arnfp8_run_share(dxs, res.to(DEV), res_out, staging, gamma.to(DEV), 1e-6, 0.0, 1200.0,
+                             ngpus=ngpus, rank=rank)
+        torch.cuda.synchronize()
+        first, count = orc_mod.share_rows(rows, ngpus, rank)
+        want = orc_mod.stage_share(q_ref, s_ref, ngpus, rank, fill=0xA5)
+        got = staging.cpu().numpy()
+        data_g = got[: S * cols].reshape(S, cols)
+        data_w = want[: S * cols].reshape(S, cols)
+        assert_fp8_close(data_g[:count], data_w[:count], min_exact=0.99)
+        assert np.all(data_g[count:] == 0xA5)
+        sc_g = got[S * cols: S * cols + 4 * count].view(np.float32)
+        assert_scales_close(sc_g, want[S * cols: S * cols + 4 * count].view(np.float32))
+        assert np.all(got[S * cols + 4 * count:] == 0xA5)
+        rb = _bits(res_out)
+        assert_bits_equal(rb[first:first + count], h_ref[first:first + count], "share residual")
+        untouched = np.ones(rows, bool)
+        untouched[first:first + count] = False
+        assert np.all(rb[untouched] == 0x40E0)  # 7.0 in bf16
+        # the share's bytes equal the single full call's rows (same kernel shape)
+        full_q = full[0].view(torch.uint8).cpu().numpy()[first:first + count]
+        assert np.array_equal(data_g[:count], full_q)
+        assert np.array_equal(sc_g, full[1].cpu().numpy()[first:first + count])
