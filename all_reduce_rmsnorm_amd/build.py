@@ -10,7 +10,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "arnfp8.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "arnfp8.hip")]  # includes csrc/arnfp8_kernels.hpp
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libarnfp8.so")
 ARCH = os.environ.get("ARNFP8_OFFLOAD_ARCH", "gfx950")

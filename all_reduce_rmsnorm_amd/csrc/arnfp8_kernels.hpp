@@ -1,0 +1,286 @@
+// arnfp8_kernels.hpp -- gfx950 (CDNA4) device code of the fused all-reduce
+// epilogue: the rank-order sum kernel and the fused row kernel.  Included by
+// arnfp8.hip (the C ABI); nothing here is visible outside that translation unit.
+//
+// Sources: Modular Mojo API docs "allreduce_rmsnorm_fp8" (function summary,
+// Args); b12x PR #283 "PCIeTwoShotBF16" (PR description); TensorRT-LLM PR
+// #19836 (Description, RESIDUAL_RMS_NORM); tt-metal rmsnorm_2d.py
+// (add_unit_offset).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "arnfp8.h"
+
+namespace arnfp8 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4m3Max = 448.0f;
+constexpr float kScaleFloor = 1.0f / 229376.0f;  // 1 / (448 * 512)
+
+struct Slabs {
+  const u32x4 *p[ARNFP8_MAX_P];
+};
+
+// ---------------------------------------------------------------- helpers --
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two fp32 -> one word of two bf16 (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight fp32 (already clamped to +-448) -> eight e4m3fn bytes, element k in
+// byte k, round to nearest even.
+__device__ __forceinline__ u32x2 pack_e4m3(const float v[8]) {
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
+  return (u32x2){(uint32_t)w0, (uint32_t)w1};
+}
+
+// Streaming accesses: every slab, residual and output byte is touched once,
+// so loads and stores are non-temporal (they do not displace gamma in cache).
+__device__ __forceinline__ u32x4 load16(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store16(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store8(u32x2 *p, u32x2 v) { __builtin_nontemporal_store(v, p); }
+
+// Rank-order sum of one chunk: rank 0's value starts the fp32 accumulator,
+// ranks 1..P-1 are added in order, and the total is rounded once to bf16.
+template <int P>
+__device__ __forceinline__ u32x4 rank_order_sum(const u32x4 (&x)[P]) {
+  float acc[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    acc[2 * w] = bf16_lo(x[0][w]);
+    acc[2 * w + 1] = bf16_hi(x[0][w]);
+  }
+#pragma unroll
+  for (int p = 1; p < P; ++p) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc[2 * w] += bf16_lo(x[p][w]);
+      acc[2 * w + 1] += bf16_hi(x[p][w]);
+    }
+  }
+  u32x4 s;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) s[w] = pack_bf16(acc[2 * w], acc[2 * w + 1]);
+  return s;
+}
+
+// h = bf16(fp32(s) + fp32(r)), elementwise on a chunk.
+__device__ __forceinline__ u32x4 add_bf16(u32x4 s, u32x4 r) {
+  u32x4 h;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    h[w] = pack_bf16(bf16_lo(s[w]) + bf16_lo(r[w]), bf16_hi(s[w]) + bf16_hi(r[w]));
+  return h;
+}
+
+// Butterfly reductions across the 64 lanes of a wave; every lane gets the result.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------- kernels --
+
+// Sum only: a flat grid-stride stream over all 16-byte chunks of the tensor.
+template <int P, int U>
+__global__ __launch_bounds__(256) void arn_sum_kernel(Slabs in, u32x4 *__restrict__ out,
+                                                      int64_t n16) {
+  const int64_t T = blockDim.x;
+  const int64_t stride = (int64_t)gridDim.x * T * U;
+  for (int64_t base = (int64_t)blockIdx.x * T * U + threadIdx.x; base < n16; base += stride) {
+    u32x4 x[U][P];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = base + u * T;
+      if (c < n16) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) x[u][p] = load16(in.p[p] + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = base + u * T;
+      if (c < n16) store16(out + c, rank_order_sum<P>(x[u]));
+    }
+  }
+}
+
+struct RowArgs {
+  Slabs in;
+  const u32x4 *res_in;
+  u32x4 *res_out;
+  u32x2 *out;  // 8 fp8 per chunk
+  float *scales;
+  const u32x4 *gamma;
+  float eps, woff, ub;
+  float cols_f;
+  int64_t rows;
+  int c16;  // 16-byte chunks per row
+};
+
+// Loads in flight per lane in the statistics pass: chunks are processed in
+// groups of G whose P slab loads (plus residual and gamma) are all issued
+// before any of them is consumed.
+// The budget is 24 loads (96 VGPRs), less what the fp32 h*g values of the
+// row (8 VGPRs per chunk) leave free under ~200 VGPRs.
+template <int P, int VPT, bool RES_IN>
+constexpr int load_group() {
+  const int budget = (200 - 8 * VPT) / 4 < 24 ? (200 - 8 * VPT) / 4 : 24;
+  int g = 1;
+  while (g * 2 <= VPT && g * 2 * (P + 1 + (RES_IN ? 1 : 0)) <= budget) g *= 2;
+  return g;
+}
+
+// fl32(h * (g + weight_offset)) for the two bf16 elements of one word; the
+// statistics and the quantisation pass both use exactly this expression.
+__device__ __forceinline__ void gain2(uint32_t h, uint32_t g, float woff, float &lo, float &hi) {
+  lo = bf16_lo(h) * (bf16_lo(g) + woff);
+  hi = bf16_hi(h) * (bf16_hi(g) + woff);
+}
+
+// Fused epilogue: workgroups walk the rows grid-stride; lane t owns chunks
+// t + v*T (v < VPT) of the row.  Between the statistics pass and the
+// quantisation pass the row stays in registers: as fp32 h*g for up to 8
+// chunks per lane, as packed bf16 h (gamma re-read from cache) for 16.
+// Chunk indices past the end of a ragged row are clamped to the row's last
+// chunk for the loads (an in-bounds duplicate read), and every store and
+// statistic of such a chunk is masked.
+template <int P, int VPT, bool RES_IN, bool RES_OUT>
+__global__ __launch_bounds__(512) void arnfp8_row_kernel(RowArgs a) {
+  constexpr int G = load_group<P, VPT, RES_IN>();
+  constexpr bool KEEP_HG = VPT <= 8;
+  __shared__ float red[2][8][2];  // [row parity][wave][sum h^2, max |h g|]
+  const int t = threadIdx.x;
+  const int T = blockDim.x;
+  const int wave = t >> 6;
+  const int nwaves = T >> 6;
+  const int last = a.c16 - 1;
+  int parity = 0;
+
+  for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
+    // Row-uniform bases (scalar registers); lanes add a 32-bit chunk index.
+    const int64_t base = row * (int64_t)a.c16;
+    const u32x4 *xs[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) xs[p] = a.in.p[p] + base;
+    const u32x4 *rin = RES_IN ? a.res_in + base : nullptr;
+    u32x4 *rout = RES_OUT ? a.res_out + base : nullptr;
+    u32x2 *qout = a.out + base;
+    float hg[KEEP_HG ? VPT : 1][8];
+    u32x4 hk[KEEP_HG ? 1 : VPT];
+    float ss = 0.0f, mx = 0.0f;
+
+#pragma unroll
+    for (int v0 = 0; v0 < VPT; v0 += G) {
+      u32x4 x[G][P], r[G], g[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int c = min((v0 + k) * T + t, last);
+#pragma unroll
+        for (int p = 0; p < P; ++p) x[k][p] = load16(xs[p] + c);
+        if constexpr (RES_IN) r[k] = load16(rin + c);
+        g[k] = a.gamma[c];
+      }
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int v = v0 + k;
+        const bool valid = v * T + t <= last;
+        u32x4 hv = rank_order_sum<P>(x[k]);
+        if constexpr (RES_IN) hv = add_bf16(hv, r[k]);
+        if constexpr (RES_OUT) {
+          if (valid) store16(rout + v * T + t, hv);
+        }
+        if constexpr (!KEEP_HG) hk[v] = hv;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          float y0, y1;
+          gain2(hv[w], g[k][w], a.woff, y0, y1);
+          if constexpr (KEEP_HG) {
+            hg[v][2 * w] = y0;
+            hg[v][2 * w + 1] = y1;
+          }
+          if (valid) {
+            const float h0 = bf16_lo(hv[w]), h1 = bf16_hi(hv[w]);
+            ss += h0 * h0;
+            ss += h1 * h1;
+            mx = fmaxf(mx, fmaxf(fabsf(y0), fabsf(y1)));
+          }
+        }
+      }
+      // Keep the next group's loads below this point: hoisting them would
+      // hold more loads in registers than the budget allows.
+      if constexpr (G < VPT) __builtin_amdgcn_sched_barrier(0);
+    }
+
+    ss = wave_sum(ss);
+    mx = wave_max(mx);
+    if ((t & 63) == 0) {
+      red[parity][wave][0] = ss;
+      red[parity][wave][1] = mx;
+    }
+    __syncthreads();
+    float tot = 0.0f, m = 0.0f;
+    for (int w = 0; w < nwaves; ++w) {
+      tot += red[parity][w][0];
+      m = fmaxf(m, red[parity][w][1]);
+    }
+
+    const float r = 1.0f / sqrtf(tot / a.cols_f + a.eps);
+    const float amax = m * r;
+    const float scale = fmaxf(fminf(amax, a.ub) / kE4m3Max, kScaleFloor);
+    const float cq = r / scale;
+    if (t == 0) a.scales[row] = scale;
+
+    constexpr int QG = KEEP_HG ? 1 : 4;  // gamma re-reads issued together
+#pragma unroll
+    for (int v0 = 0; v0 < VPT; v0 += QG) {
+      u32x4 g[QG];
+      if constexpr (!KEEP_HG) {
+#pragma unroll
+        for (int k = 0; k < QG; ++k) g[k] = a.gamma[min((v0 + k) * T + t, last)];
+      }
+      if constexpr (!KEEP_HG) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < QG; ++k) {
+        const int v = v0 + k;
+        const int c = v * T + t;
+        float y[8];
+        if constexpr (KEEP_HG) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = hg[v][e];
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) gain2(hk[v][w], g[k][w], a.woff, y[2 * w], y[2 * w + 1]);
+        }
+        if (c <= last) {
+          float q[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = fminf(fmaxf(y[e] * cq, -kE4m3Max), kE4m3Max);
+          store8(qout + c, pack_e4m3(q));
+        }
+      }
+    }
+  }
+}
+
+}  // namespace arnfp8

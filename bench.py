@@ -41,8 +41,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 DEFAULT_WORKLOAD = "prefill_p8_8192x7168"
 DECODE_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "tiny_p2_4x256"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8.hip"),
-                  os.path.join(ROOT, "include", "arnfp8.h"),
+# The device code and the flags it is built with: the committed HBM-counter
+# summary applies only while these are unchanged.
+KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_kernels.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
 
 

@@ -68,6 +68,21 @@ def lib() -> ctypes.CDLL:
         L.oracle_arnfp8.argtypes = [ctypes.POINTER(_u16p), ctypes.c_int, _u16p, _u16p,
                                     _u8p, _f32p, _u16p, ctypes.c_float, ctypes.c_float,
                                     ctypes.c_float, ctypes.c_int64, ctypes.c_int64]
+        L.oracle_arnfp8_e5m2.restype = ctypes.c_int
+        L.oracle_arnfp8_e5m2.argtypes = L.oracle_arnfp8.argtypes
+        _f64p = ctypes.POINTER(ctypes.c_double)
+        L.oracle_norm_rows.restype = ctypes.c_int
+        L.oracle_norm_rows.argtypes = [ctypes.POINTER(_u16p), ctypes.c_int, _u16p, _u16p, _u16p,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_int64,
+                                       ctypes.c_int64, _f64p]
+        L.oracle_mx_shared_exp.restype = ctypes.c_int
+        L.oracle_mx_shared_exp.argtypes = [_f64p, ctypes.c_int]
+        L.oracle_mx_quantize_block.restype = None
+        L.oracle_mx_quantize_block.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, _u8p]
+        L.oracle_arnfp8_mx.restype = ctypes.c_int
+        L.oracle_arnfp8_mx.argtypes = [ctypes.POINTER(_u16p), ctypes.c_int, _u16p, _u16p, _u8p,
+                                       _u8p, _u16p, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_int64, ctypes.c_int64]
         L.oracle_share_rows.restype = None
         L.oracle_share_rows.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int64),
@@ -140,6 +155,79 @@ def sum_bf16(inputs) -> np.ndarray:
     if st != 0:
         raise ValueError(f"oracle_sum_bf16 failed with status {st}")
     return out
+
+
+def _fused(fn, inputs, gamma, eps, weight_offset, scale_ub, residual_in, want_residual_out):
+    arrs, ptrs, shape = _slabs(inputs)
+    rows, cols = _rows_cols(shape)
+    gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+    assert gamma.shape == (cols,)
+    res_in = None
+    if residual_in is not None:
+        res_in = np.ascontiguousarray(residual_in, dtype=np.uint16)
+        assert res_in.shape == shape
+    res_out = np.empty(shape, dtype=np.uint16) if want_residual_out else None
+    out = np.empty(shape, dtype=np.uint8)
+    scales = np.empty((rows,), dtype=np.float32)
+    st = fn(ptrs, len(arrs), _ptr(res_in, _u16p), _ptr(res_out, _u16p), _ptr(out, _u8p),
+            _ptr(scales, _f32p), _ptr(gamma, _u16p), float(eps), float(weight_offset),
+            float(scale_ub), rows, cols)
+    if st != 0:
+        raise ValueError(f"oracle fused call failed with status {st}")
+    return out, scales, res_out
+
+
+def arnfp8_e5m2(inputs, gamma, eps, weight_offset, scale_ub, residual_in=None,
+                want_residual_out=True):
+    """The fused epilogue with e5m2 output (per-row scale over 57344)."""
+    return _fused(lib().oracle_arnfp8_e5m2, inputs, gamma, eps, weight_offset, scale_ub,
+                  residual_in, want_residual_out)
+
+
+def norm_rows(inputs, gamma, eps, weight_offset, residual_in=None):
+    """The normalised rows y = h * r * g in fp64 (steps up to the norm)."""
+    arrs, ptrs, shape = _slabs(inputs)
+    rows, cols = _rows_cols(shape)
+    gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+    res_in = None if residual_in is None else np.ascontiguousarray(residual_in, dtype=np.uint16)
+    y = np.empty((rows, cols), dtype=np.float64)
+    st = lib().oracle_norm_rows(ptrs, len(arrs), _ptr(res_in, _u16p), _ptr(None, _u16p),
+                                _ptr(gamma, _u16p), float(eps), float(weight_offset), rows, cols,
+                                y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    if st != 0:
+        raise ValueError(f"oracle_norm_rows failed with status {st}")
+    return y
+
+
+def mx_shared_exp(block) -> int:
+    v = np.ascontiguousarray(block, dtype=np.float64)
+    return lib().oracle_mx_shared_exp(v.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), v.size)
+
+
+def mx_quantize_block(block, shared_exp: int) -> np.ndarray:
+    v = np.ascontiguousarray(block, dtype=np.float64)
+    codes = np.empty(v.size, dtype=np.uint8)
+    lib().oracle_mx_quantize_block(v.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), v.size,
+                                   int(shared_exp), _ptr(codes, _u8p))
+    return codes
+
+
+def arnfp8_mx(inputs, gamma, eps, weight_offset, residual_in=None, want_residual_out=True):
+    """The fused epilogue with MXFP8 output: (codes u8 [rows, cols], E8M0 block
+    scales u8 [rows, cols / 32], residual_out u16 or None)."""
+    arrs, ptrs, shape = _slabs(inputs)
+    rows, cols = _rows_cols(shape)
+    gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+    res_in = None if residual_in is None else np.ascontiguousarray(residual_in, dtype=np.uint16)
+    res_out = np.empty(shape, dtype=np.uint16) if want_residual_out else None
+    out = np.empty(shape, dtype=np.uint8)
+    bs = np.empty((rows, cols // 32), dtype=np.uint8)
+    st = lib().oracle_arnfp8_mx(ptrs, len(arrs), _ptr(res_in, _u16p), _ptr(res_out, _u16p),
+                                _ptr(out, _u8p), _ptr(bs, _u8p), _ptr(gamma, _u16p), float(eps),
+                                float(weight_offset), rows, cols)
+    if st != 0:
+        raise ValueError(f"oracle_arnfp8_mx failed with status {st}")
+    return out, bs, res_out
 
 
 def arnfp8(inputs, gamma, eps, weight_offset, scale_ub, residual_in=None,

@@ -207,11 +207,50 @@ int oracle_sum_bf16(const uint16_t *const *inputs, int P, uint16_t *out,
     return ORACLE_OK;
 }
 
-int oracle_arnfp8(const uint16_t *const *inputs, int P,
-                  const uint16_t *residual_in, uint16_t *residual_out,
-                  uint8_t *out_fp8, float *scales, const uint16_t *gamma,
-                  float eps, float weight_offset, float scale_ub,
-                  int64_t rows, int64_t cols)
+/* Steps S1-S5 for row i: sum, optional residual add and write-back, and the
+ * normalised row y = h * r * g in fp64.  `h` and `y` hold `cols` doubles. */
+static void norm_row(const uint16_t *const *inputs, int P, const uint16_t *residual_in,
+                     uint16_t *residual_out, const uint16_t *gamma, float eps,
+                     float weight_offset, int64_t i, int64_t cols, double *h, double *y)
+{
+    /* Sum, optional residual add, residual write-back. */
+    for (int64_t j = 0; j < cols; ++j) {
+        int64_t k = i * cols + j;
+        uint16_t hb = rank_order_sum(inputs, P, k);
+        if (residual_in != NULL) {
+            float t = oracle_bf16_to_f32(hb) + oracle_bf16_to_f32(residual_in[k]);
+            hb = oracle_f32_to_bf16(t);
+        }
+        if (residual_out != NULL)
+            residual_out[k] = hb;
+        h[j] = (double)oracle_bf16_to_f32(hb);
+    }
+
+    /* RMSNorm: r = 1 / sqrt(mean(h^2) + eps), y = h * r * g. */
+    double sumsq = 0.0;
+    for (int64_t j = 0; j < cols; ++j)
+        sumsq += h[j] * h[j];
+    double ms = sumsq / (double)cols;
+    double r = 1.0 / sqrt(ms + (double)eps);
+
+    for (int64_t j = 0; j < cols; ++j) {
+        float g = oracle_bf16_to_f32(gamma[j]) + weight_offset; /* fp32 add */
+        y[j] = h[j] * r * (double)g;
+    }
+}
+
+/* Per-row scale: amax clamped at scale_ub, over the format's maximum `fmax`,
+ * floored at 1 / (fmax * 512); all in fp32 (fmax * 512 is exact). */
+static float row_scale(float amax, float scale_ub, float fmax)
+{
+    return fmaxf(fminf(amax, scale_ub) / fmax, 1.0f / (fmax * 512.0f));
+}
+
+/* The per-row dynamic quantisation shared by the e4m3fn and e5m2 outputs. */
+static int fused_per_row(const uint16_t *const *inputs, int P, const uint16_t *residual_in,
+                         uint16_t *residual_out, uint8_t *out_fp8, float *scales,
+                         const uint16_t *gamma, float eps, float weight_offset,
+                         float scale_ub, int64_t rows, int64_t cols, int e5m2)
 {
     int st = check_common(inputs, P, rows, cols);
     if (st != ORACLE_OK)
@@ -219,6 +258,7 @@ int oracle_arnfp8(const uint16_t *const *inputs, int P,
     if (out_fp8 == NULL || scales == NULL || gamma == NULL)
         return ORACLE_BAD_ARG;
 
+    const float fmax = e5m2 ? 57344.0f : 448.0f;
     double *h = (double *)malloc((size_t)cols * sizeof(double));
     double *y = (double *)malloc((size_t)cols * sizeof(double));
     if (h == NULL || y == NULL) {
@@ -228,51 +268,138 @@ int oracle_arnfp8(const uint16_t *const *inputs, int P,
     }
 
     for (int64_t i = 0; i < rows; ++i) {
-        /* Sum, optional residual add, residual write-back. */
-        for (int64_t j = 0; j < cols; ++j) {
-            int64_t k = i * cols + j;
-            uint16_t hb = rank_order_sum(inputs, P, k);
-            if (residual_in != NULL) {
-                float t = oracle_bf16_to_f32(hb) + oracle_bf16_to_f32(residual_in[k]);
-                hb = oracle_f32_to_bf16(t);
-            }
-            if (residual_out != NULL)
-                residual_out[k] = hb;
-            h[j] = (double)oracle_bf16_to_f32(hb);
-        }
-
-        /* RMSNorm: r = 1 / sqrt(mean(h^2) + eps), y = h * r * g. */
-        double sumsq = 0.0;
-        for (int64_t j = 0; j < cols; ++j)
-            sumsq += h[j] * h[j];
-        double ms = sumsq / (double)cols;
-        double r = 1.0 / sqrt(ms + (double)eps);
+        norm_row(inputs, P, residual_in, residual_out, gamma, eps, weight_offset, i, cols, h, y);
 
         double ymax = 0.0;
-        for (int64_t j = 0; j < cols; ++j) {
-            float g = oracle_bf16_to_f32(gamma[j]) + weight_offset; /* fp32 add */
-            y[j] = h[j] * r * (double)g;
+        for (int64_t j = 0; j < cols; ++j)
             if (fabs(y[j]) > ymax)
                 ymax = fabs(y[j]);
-        }
-
-        /* Per-row scale: amax clamped at scale_ub, over the e4m3fn maximum,
-         * floored at 1 / (448 * 512); all in fp32. */
         float amax = (float)ymax;
-        float scale = fmaxf(fminf(amax, scale_ub) / 448.0f, 1.0f / 229376.0f);
+        float scale = row_scale(amax, scale_ub, fmax);
         scales[i] = scale;
 
         /* Quantise: the code is decided from the fp32 value y / scale. */
         for (int64_t j = 0; j < cols; ++j) {
             float v = (float)(y[j] / (double)scale);
-            if (v > 448.0f)
-                v = 448.0f;
-            if (v < -448.0f)
-                v = -448.0f;
-            out_fp8[i * cols + j] = oracle_f32_to_e4m3fn_sat(v);
+            if (v > fmax)
+                v = fmax;
+            if (v < -fmax)
+                v = -fmax;
+            out_fp8[i * cols + j] = e5m2 ? oracle_f32_to_e5m2_sat(v) : oracle_f32_to_e4m3fn_sat(v);
         }
     }
 
+    free(h);
+    free(y);
+    return ORACLE_OK;
+}
+
+int oracle_arnfp8(const uint16_t *const *inputs, int P,
+                  const uint16_t *residual_in, uint16_t *residual_out,
+                  uint8_t *out_fp8, float *scales, const uint16_t *gamma,
+                  float eps, float weight_offset, float scale_ub,
+                  int64_t rows, int64_t cols)
+{
+    return fused_per_row(inputs, P, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                         weight_offset, scale_ub, rows, cols, 0);
+}
+
+int oracle_arnfp8_e5m2(const uint16_t *const *inputs, int P,
+                       const uint16_t *residual_in, uint16_t *residual_out,
+                       uint8_t *out_fp8, float *scales, const uint16_t *gamma,
+                       float eps, float weight_offset, float scale_ub,
+                       int64_t rows, int64_t cols)
+{
+    return fused_per_row(inputs, P, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                         weight_offset, scale_ub, rows, cols, 1);
+}
+
+int oracle_norm_rows(const uint16_t *const *inputs, int P, const uint16_t *residual_in,
+                     uint16_t *residual_out, const uint16_t *gamma, float eps,
+                     float weight_offset, int64_t rows, int64_t cols, double *y)
+{
+    int st = check_common(inputs, P, rows, cols);
+    if (st != ORACLE_OK)
+        return st;
+    if (gamma == NULL || y == NULL)
+        return ORACLE_BAD_ARG;
+    double *h = (double *)malloc((size_t)cols * sizeof(double));
+    if (h == NULL)
+        return ORACLE_NO_MEMORY;
+    for (int64_t i = 0; i < rows; ++i)
+        norm_row(inputs, P, residual_in, residual_out, gamma, eps, weight_offset, i, cols, h,
+                 y + i * cols);
+    free(h);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------- MX block quantisation -- */
+/*
+ * OCP Microscaling (MX) v1.0, MXFP8 with E4M3 elements: a block of 32 values
+ * shares one power-of-two scale X = 2^e stored as an E8M0 byte (e + 127).
+ * e = floor(log2(max_i |V_i|)) - emax, with emax = 8 the exponent of the
+ * largest E4M3 normal (448 = 1.75 * 2^8); each element is V_i / X rounded to
+ * E4M3 (nearest, ties to even), saturating at +-448.  A block of zeros takes
+ * e = -127 (the smallest E8M0 scale).  The block structure follows the
+ * mx-quantisation scale shape (BS, ceil(H/64), 2) of Huawei CANN
+ * aclnnAlltoAllQuantMatmul (calculation formula): two scales per 64 values.
+ */
+
+int oracle_mx_shared_exp(const double *v, int n)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i)
+        if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    if (amax == 0.0)
+        return -127;
+    int k;
+    (void)frexp(amax, &k);  /* amax = m * 2^k, m in [0.5, 1): floor(log2) = k - 1 */
+    int e = (k - 1) - 8;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
+void oracle_mx_quantize_block(const double *v, int n, int shared_exp, uint8_t *codes)
+{
+    for (int i = 0; i < n; ++i) {
+        float q = (float)ldexp(v[i], -shared_exp); /* the decision value, in fp32 */
+        if (q > 448.0f)
+            q = 448.0f;
+        if (q < -448.0f)
+            q = -448.0f;
+        codes[i] = oracle_f32_to_e4m3fn_sat(q);
+    }
+}
+
+int oracle_arnfp8_mx(const uint16_t *const *inputs, int P,
+                     const uint16_t *residual_in, uint16_t *residual_out,
+                     uint8_t *out_fp8, uint8_t *block_scales, const uint16_t *gamma,
+                     float eps, float weight_offset, int64_t rows, int64_t cols)
+{
+    int st = check_common(inputs, P, rows, cols);
+    if (st != ORACLE_OK)
+        return st;
+    if (out_fp8 == NULL || block_scales == NULL || gamma == NULL || cols % 32 != 0)
+        return ORACLE_BAD_ARG;
+    double *h = (double *)malloc((size_t)cols * sizeof(double));
+    double *y = (double *)malloc((size_t)cols * sizeof(double));
+    if (h == NULL || y == NULL) {
+        free(h);
+        free(y);
+        return ORACLE_NO_MEMORY;
+    }
+    for (int64_t i = 0; i < rows; ++i) {
+        norm_row(inputs, P, residual_in, residual_out, gamma, eps, weight_offset, i, cols, h, y);
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            int e = oracle_mx_shared_exp(y + 32 * b, 32);
+            block_scales[i * (cols / 32) + b] = (uint8_t)(e + 127);
+            oracle_mx_quantize_block(y + 32 * b, 32, e, out_fp8 + i * cols + 32 * b);
+        }
+    }
     free(h);
     free(y);
     return ORACLE_OK;

@@ -74,6 +74,36 @@ int oracle_arnfp8(const uint16_t *const *inputs, int P,
                   float eps, float weight_offset, float scale_ub,
                   int64_t rows, int64_t cols);
 
+/* The same epilogue with e5m2 output: the format maximum 57344 replaces 448,
+ *   scale = max(min(amax, scale_ub) / 57344, 1 / (57344 * 512)),
+ *   q_j = e5m2_rne_sat(fl32(y_j / scale)). */
+int oracle_arnfp8_e5m2(const uint16_t *const *inputs, int P,
+                       const uint16_t *residual_in, uint16_t *residual_out,
+                       uint8_t *out_fp8, float *scales, const uint16_t *gamma,
+                       float eps, float weight_offset, float scale_ub,
+                       int64_t rows, int64_t cols);
+
+/* Steps up to the norm only: y [rows, cols] (fp64) = h * r * g, and
+ * residual_out as in oracle_arnfp8. */
+int oracle_norm_rows(const uint16_t *const *inputs, int P, const uint16_t *residual_in,
+                     uint16_t *residual_out, const uint16_t *gamma, float eps,
+                     float weight_offset, int64_t rows, int64_t cols, double *y);
+
+/* MXFP8 (OCP MX v1.0, E4M3 elements, blocks of 32, E8M0 scales):
+ * shared exponent of a block, floor(log2(max |v|)) - 8 clamped to [-127, 127]
+ * (-127 for an all-zero block) ... */
+int oracle_mx_shared_exp(const double *v, int n);
+/* ... and its codes: e4m3fn_rne_sat(fl32(v * 2^-shared_exp)). */
+void oracle_mx_quantize_block(const double *v, int n, int shared_exp, uint8_t *codes);
+
+/* The epilogue with MXFP8 output instead of the per-row scale: out_fp8
+ * [rows, cols] e4m3fn, block_scales [rows, cols / 32] E8M0 bytes (e + 127).
+ * cols % 32 == 0.  There is no scale_ub: MX scales are not clamped. */
+int oracle_arnfp8_mx(const uint16_t *const *inputs, int P,
+                     const uint16_t *residual_in, uint16_t *residual_out,
+                     uint8_t *out_fp8, uint8_t *block_scales, const uint16_t *gamma,
+                     float eps, float weight_offset, int64_t rows, int64_t cols);
+
 /* ---- two-stage row share and its staging layout ------------------------ */
 /*
  * In the two-stage (large payload) path each of `ngpus` ranks owns

@@ -13,7 +13,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "arnfp8_oracle.c")
-PIN_FILES = ["tests/test_oracle_sum.py", "tests/test_oracle_norm.py", "tests/test_oracle_codecs.py"]
+PIN_FILES = ["tests/test_oracle_sum.py", "tests/test_oracle_norm.py", "tests/test_oracle_codecs.py",
+             "tests/test_oracle_quant_variants.py", "tests/test_oracle_share.py"]
 
 MUTANTS = {
     "bf16_ties_away": ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
@@ -28,11 +29,19 @@ MUTANTS = {
     "gamma_reversed": ("oracle_bf16_to_f32(gamma[j])", "oracle_bf16_to_f32(gamma[cols - 1 - j])"),
     "drop_weight_offset": ("oracle_bf16_to_f32(gamma[j]) + weight_offset;", "oracle_bf16_to_f32(gamma[j]);"),
     "drop_scale_clamp": ("fminf(amax, scale_ub)", "amax"),
-    "drop_scale_floor": ("1.0f / 229376.0f);\n        scales", "0.0f);\n        scales"),
-    "fnuz_max_240": ("fminf(amax, scale_ub) / 448.0f", "fminf(amax, scale_ub) / 240.0f"),
+    "drop_scale_floor": ("1.0f / (fmax * 512.0f)", "0.0f"),
+    "fnuz_max_240": ("const float fmax = e5m2 ? 57344.0f : 448.0f;", "const float fmax = e5m2 ? 57344.0f : 240.0f;"),
     "fp8_ties_away": ("(frac == 0.5 && fmod(lo, 2.0) == 1.0)", "(frac == 0.5)"),
     "fp8_wrong_subnormal_edge": ("round_to_grid(a, -6, 3)", "round_to_grid(a, -7, 3)"),
     "sign_dropped": ("y[j] = h[j] * r * (double)g;", "y[j] = fabs(h[j]) * r * (double)g;"),
+    "e5m2_wrong_subnormal_edge": ("round_to_grid(a, -14, 2)", "round_to_grid(a, -15, 2)"),
+    "e5m2_uses_e4m3_max": ("const float fmax = e5m2 ? 57344.0f : 448.0f;", "const float fmax = 448.0f;"),
+    "mx_emax_7": ("int e = (k - 1) - 8;", "int e = (k - 1) - 7;"),
+    "mx_zero_block_exp_0": ("        return -127;\n    int k;", "        return 0;\n    int k;"),
+    "mx_amax_of_half_block": ("for (int i = 0; i < n; ++i)\n        if (fabs(v[i]) > amax)",
+                              "for (int i = 0; i < n / 2; ++i)\n        if (fabs(v[i]) > amax)"),
+    "share_floor_not_ceil": ("int64_t S = (rows + ngpus - 1) / ngpus;\n    int64_t lo", "int64_t S = rows / ngpus + 1;\n    int64_t lo"),
+    "stage_no_padding": ("(scale_bytes + simd_width - 1) / simd_width * simd_width", "scale_bytes"),
     "rsqrt_not_inverse": ("double r = 1.0 / sqrt(ms + (double)eps);", "double r = 1.0 / (ms + (double)eps);"),
 }
 
