@@ -17,7 +17,7 @@ __all__ = [
     "ArnFp8Error", "MAX_P", "MAX_COLS", "STATUS",
     "arnfp8_run", "arnfp8_run_ex", "arn_sum_bf16", "arnfp8_status_string", "Launch",
     "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW", "arnfp8_stage_bytes",
-    "arnfp8_run_share", "SIMD_WIDTH",
+    "arnfp8_run_share", "SIMD_WIDTH", "arnfp8_run_fmt", "FMT_E4M3FN", "FMT_E5M2", "FMT_MXFP8",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -28,8 +28,11 @@ MAX_COLS = 65536
 STATUS = {
     0: "ARNFP8_OK", 1: "ARNFP8_NULL_POINTER", 2: "ARNFP8_MISALIGNED", 3: "ARNFP8_BAD_SHAPE",
     4: "ARNFP8_BAD_P", 5: "ARNFP8_ALIAS", 6: "ARNFP8_HIP_ERROR", 7: "ARNFP8_BAD_CONFIG",
-    8: "ARNFP8_BAD_SHARE",
+    8: "ARNFP8_BAD_SHARE", 9: "ARNFP8_BAD_FORMAT",
 }
+FMT_E4M3FN = 0
+FMT_E5M2 = 1
+FMT_MXFP8 = 2
 SIMD_WIDTH = 16
 
 
@@ -76,6 +79,10 @@ def library() -> ctypes.CDLL:
         L.arnfp8_run_ex.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
                                     ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int, vp,
                                     ctypes.POINTER(Launch)]
+        L.arnfp8_run_fmt.restype = ctypes.c_int
+        L.arnfp8_run_fmt.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
+                                     ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int,
+                                     ctypes.c_int, vp, ctypes.POINTER(Launch)]
         L.arnfp8_stage_bytes.restype = ctypes.c_int64
         L.arnfp8_stage_bytes.argtypes = [i64, i64, ctypes.c_int]
         L.arnfp8_run_share.restype = ctypes.c_int
@@ -188,3 +195,21 @@ def arnfp8_run_share(inputs, residual_in, residual_out, staging, gamma, eps, wei
                                     _stream(stream))
     if st != 0:
         raise ArnFp8Error("arnfp8_run_share", st)
+
+
+def arnfp8_run_fmt(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps, weight_offset,
+                   scale_ub, out_format=FMT_E4M3FN, rows=None, cols=None, P=None, stream=None,
+                   launch=None) -> None:
+    """The fused epilogue with output format ``out_format`` (FMT_E4M3FN,
+    FMT_E5M2: fp32 per-row ``scales``; FMT_MXFP8: uint8 E8M0 ``scales``
+    [rows, cols / 32])."""
+    rows, cols, P = _shape(inputs, rows, cols, P)
+    if isinstance(launch, dict):
+        launch = Launch(**launch)
+    opt = ctypes.byref(launch) if launch is not None else None
+    st = library().arnfp8_run_fmt(_ptr_array(inputs), _ptr(residual_in), _ptr(residual_out),
+                                  _ptr(out_fp8), _ptr(scales), _ptr(gamma), float(eps),
+                                  float(weight_offset), float(scale_ub), rows, cols, P,
+                                  int(out_format), _stream(stream), opt)
+    if st != 0:
+        raise ArnFp8Error("arnfp8_run_fmt", st)

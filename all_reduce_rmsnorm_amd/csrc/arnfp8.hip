@@ -104,33 +104,45 @@ SumKernel sum_table(int P) {
 
 typedef void (*RowKernel)(RowArgs);
 
-template <int P, int VPT>
+template <int FMT, int P, int VPT>
 RowKernel row_kernel_res(bool res_in, bool res_out) {
-  if (res_in) return res_out ? arnfp8_row_kernel<P, VPT, true, true> : arnfp8_row_kernel<P, VPT, true, false>;
-  return res_out ? arnfp8_row_kernel<P, VPT, false, true> : arnfp8_row_kernel<P, VPT, false, false>;
+  if (res_in)
+    return res_out ? arnfp8_row_kernel<FMT, P, VPT, true, true>
+                   : arnfp8_row_kernel<FMT, P, VPT, true, false>;
+  return res_out ? arnfp8_row_kernel<FMT, P, VPT, false, true>
+                 : arnfp8_row_kernel<FMT, P, VPT, false, false>;
 }
 
-template <int P>
+template <int FMT, int P>
 RowKernel row_kernel_vpt(int vpt, bool res_in, bool res_out) {
   switch (vpt) {
-    case 1: return row_kernel_res<P, 1>(res_in, res_out);
-    case 2: return row_kernel_res<P, 2>(res_in, res_out);
-    case 4: return row_kernel_res<P, 4>(res_in, res_out);
-    case 8: return row_kernel_res<P, 8>(res_in, res_out);
-    default: return row_kernel_res<P, 16>(res_in, res_out);
+    case 1: return row_kernel_res<FMT, P, 1>(res_in, res_out);
+    case 2: return row_kernel_res<FMT, P, 2>(res_in, res_out);
+    case 4: return row_kernel_res<FMT, P, 4>(res_in, res_out);
+    case 8: return row_kernel_res<FMT, P, 8>(res_in, res_out);
+    default: return row_kernel_res<FMT, P, 16>(res_in, res_out);
   }
 }
 
-RowKernel row_table(int P, int vpt, bool res_in, bool res_out) {
+template <int FMT>
+RowKernel row_kernel_p(int P, int vpt, bool res_in, bool res_out) {
   switch (P) {
-    case 1: return row_kernel_vpt<1>(vpt, res_in, res_out);
-    case 2: return row_kernel_vpt<2>(vpt, res_in, res_out);
-    case 3: return row_kernel_vpt<3>(vpt, res_in, res_out);
-    case 4: return row_kernel_vpt<4>(vpt, res_in, res_out);
-    case 5: return row_kernel_vpt<5>(vpt, res_in, res_out);
-    case 6: return row_kernel_vpt<6>(vpt, res_in, res_out);
-    case 7: return row_kernel_vpt<7>(vpt, res_in, res_out);
-    default: return row_kernel_vpt<8>(vpt, res_in, res_out);
+    case 1: return row_kernel_vpt<FMT, 1>(vpt, res_in, res_out);
+    case 2: return row_kernel_vpt<FMT, 2>(vpt, res_in, res_out);
+    case 3: return row_kernel_vpt<FMT, 3>(vpt, res_in, res_out);
+    case 4: return row_kernel_vpt<FMT, 4>(vpt, res_in, res_out);
+    case 5: return row_kernel_vpt<FMT, 5>(vpt, res_in, res_out);
+    case 6: return row_kernel_vpt<FMT, 6>(vpt, res_in, res_out);
+    case 7: return row_kernel_vpt<FMT, 7>(vpt, res_in, res_out);
+    default: return row_kernel_vpt<FMT, 8>(vpt, res_in, res_out);
+  }
+}
+
+RowKernel row_table(int fmt, int P, int vpt, bool res_in, bool res_out) {
+  switch (fmt) {
+    case ARNFP8_FMT_E5M2: return row_kernel_p<kFmtE5m2>(P, vpt, res_in, res_out);
+    case ARNFP8_FMT_MXFP8: return row_kernel_p<kFmtMx>(P, vpt, res_in, res_out);
+    default: return row_kernel_p<kFmtE4m3>(P, vpt, res_in, res_out);
   }
 }
 
@@ -159,13 +171,14 @@ RowConfig pick_row_config(int64_t rows, int c16) {
 
 // Validates the fused call's arguments and fills the kernel arguments.
 int prepare_fused(const void *const *inputs, const void *residual_in, void *residual_out,
-                  void *out_fp8, float *scales, const void *gamma, float eps,
+                  void *out_fp8, void *scales, const void *gamma, float eps,
                   float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
-                  RowArgs *a) {
+                  RowArgs *a, int fmt = ARNFP8_FMT_E4M3FN) {
   int st = check_inputs(inputs, P);
   if (st != ARNFP8_OK) return st;
   if (out_fp8 == nullptr || scales == nullptr || gamma == nullptr) return ARNFP8_NULL_POINTER;
-  if (!aligned(out_fp8, 16) || !aligned(gamma, 16) || !aligned(scales, 4) ||
+  if (!aligned(out_fp8, 16) || !aligned(gamma, 16) ||
+      !aligned(scales, fmt == ARNFP8_FMT_MXFP8 ? 1 : 4) ||
       (residual_in && !aligned(residual_in, 16)) || (residual_out && !aligned(residual_out, 16)))
     return ARNFP8_MISALIGNED;
 
@@ -181,7 +194,9 @@ int prepare_fused(const void *const *inputs, const void *residual_in, void *resi
   Range outs[3];
   int nout = 0;
   outs[nout++] = Range{(uintptr_t)out_fp8, (uintptr_t)out_fp8 + n};
-  outs[nout++] = Range{(uintptr_t)scales, (uintptr_t)scales + 4 * (uintptr_t)rows};
+  const uintptr_t scale_bytes =
+      fmt == ARNFP8_FMT_MXFP8 ? (uintptr_t)(rows * (cols / 32)) : 4 * (uintptr_t)rows;
+  outs[nout++] = Range{(uintptr_t)scales, (uintptr_t)scales + scale_bytes};
   const int res_out_slot = residual_out ? nout : -1;
   if (residual_out) outs[nout++] = Range{(uintptr_t)residual_out, (uintptr_t)residual_out + 2 * n};
   for (int o = 0; o < nout; ++o) {
@@ -197,7 +212,8 @@ int prepare_fused(const void *const *inputs, const void *residual_in, void *resi
   a->res_in = (const u32x4 *)residual_in;
   a->res_out = (u32x4 *)residual_out;
   a->out = (u32x2 *)out_fp8;
-  a->scales = scales;
+  a->scales = fmt == ARNFP8_FMT_MXFP8 ? nullptr : (float *)scales;
+  a->mx_scales = fmt == ARNFP8_FMT_MXFP8 ? (uint8_t *)scales : nullptr;
   a->gamma = (const u32x4 *)gamma;
   a->eps = eps;
   a->woff = weight_offset;
@@ -269,23 +285,37 @@ extern "C" int arn_sum_bf16(const void *const *inputs, void *out, int64_t rows, 
   return launch_status();
 }
 
-extern "C" int arnfp8_run_ex(const void *const *inputs, const void *residual_in,
-                             void *residual_out, void *out_fp8, float *scales, const void *gamma,
-                             float eps, float weight_offset, float scale_ub, int64_t rows,
-                             int64_t cols, int P, hipStream_t stream, const arnfp8_launch *opt) {
+extern "C" int arnfp8_run_fmt(const void *const *inputs, const void *residual_in,
+                              void *residual_out, void *out_fp8, void *scales, const void *gamma,
+                              float eps, float weight_offset, float scale_ub, int64_t rows,
+                              int64_t cols, int P, int out_format, hipStream_t stream,
+                              const arnfp8_launch *opt) {
   int st = check_shape(rows, cols, P);
   if (st != ARNFP8_OK) return st;
+  if (out_format != ARNFP8_FMT_E4M3FN && out_format != ARNFP8_FMT_E5M2 &&
+      out_format != ARNFP8_FMT_MXFP8)
+    return ARNFP8_BAD_FORMAT;
+  if (out_format == ARNFP8_FMT_MXFP8 && cols % 32 != 0) return ARNFP8_BAD_SHAPE;
   RowConfig cfg;
   st = resolve_row_config(opt, rows, (int)(cols / 8), &cfg);
   if (st != ARNFP8_OK) return st;
   if (rows == 0) return ARNFP8_OK;
   RowArgs a;
   st = prepare_fused(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
-                     weight_offset, scale_ub, rows, cols, P, &a);
+                     weight_offset, scale_ub, rows, cols, P, &a, out_format);
   if (st != ARNFP8_OK) return st;
-  hipLaunchKernelGGL(row_table(P, cfg.vpt, residual_in != nullptr, residual_out != nullptr),
+  hipLaunchKernelGGL(row_table(out_format, P, cfg.vpt, residual_in != nullptr,
+                               residual_out != nullptr),
                      dim3(cfg.grid), dim3(cfg.threads), 0, stream, a);
   return launch_status();
+}
+
+extern "C" int arnfp8_run_ex(const void *const *inputs, const void *residual_in,
+                             void *residual_out, void *out_fp8, float *scales, const void *gamma,
+                             float eps, float weight_offset, float scale_ub, int64_t rows,
+                             int64_t cols, int P, hipStream_t stream, const arnfp8_launch *opt) {
+  return arnfp8_run_fmt(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                        weight_offset, scale_ub, rows, cols, P, ARNFP8_FMT_E4M3FN, stream, opt);
 }
 
 extern "C" int arnfp8_run(const void *const *inputs, const void *residual_in, void *residual_out,
@@ -356,7 +386,8 @@ extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_
   st = prepare_fused(shifted, rin, rout, out, scales, gamma, eps, weight_offset, scale_ub, count,
                      cols, P, &a);
   if (st != ARNFP8_OK) return st;
-  hipLaunchKernelGGL(row_table(P, cfg.vpt, residual_in != nullptr, residual_out != nullptr),
+  hipLaunchKernelGGL(row_table(ARNFP8_FMT_E4M3FN, P, cfg.vpt, residual_in != nullptr,
+                               residual_out != nullptr),
                      dim3(cfg.grid), dim3(cfg.threads), 0, stream, a);
   return launch_status();
 }
@@ -372,6 +403,7 @@ extern "C" const char *arnfp8_status_string(int status) {
     case ARNFP8_HIP_ERROR: return "HIP launch error";
     case ARNFP8_BAD_CONFIG: return "invalid launch configuration";
     case ARNFP8_BAD_SHARE: return "bad share: ngpus must be >= 1 and 0 <= rank < ngpus";
+    case ARNFP8_BAD_FORMAT: return "unknown output format";
     default: return "unknown status";
   }
 }

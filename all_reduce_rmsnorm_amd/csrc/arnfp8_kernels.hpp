@@ -20,8 +20,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kE4m3Max = 448.0f;
-constexpr float kScaleFloor = 1.0f / 229376.0f;  // 1 / (448 * 512)
+// Output formats of the fused kernel.
+constexpr int kFmtE4m3 = ARNFP8_FMT_E4M3FN;  // per-row fp32 scale, OCP e4m3fn
+constexpr int kFmtE5m2 = ARNFP8_FMT_E5M2;    // per-row fp32 scale, OCP e5m2
+constexpr int kFmtMx = ARNFP8_FMT_MXFP8;     // e4m3fn + one E8M0 scale per 32 values
+
+// Largest finite value of the per-row formats; the row scale is floored at
+// 1 / (fmax * 512).
+template <int FMT>
+constexpr float fmt_max() { return FMT == kFmtE5m2 ? 57344.0f : 448.0f; }
+template <int FMT>
+constexpr float fmt_floor() { return 1.0f / (fmt_max<FMT>() * 512.0f); }
 
 struct Slabs {
   const u32x4 *p[ARNFP8_MAX_P];
@@ -48,6 +57,24 @@ __device__ __forceinline__ u32x2 pack_e4m3(const float v[8]) {
   return (u32x2){(uint32_t)w0, (uint32_t)w1};
 }
 
+// The same for OCP e5m2 (the gfx950 "bf8" conversion), values clamped to
+// +-57344.
+__device__ __forceinline__ u32x2 pack_e5m2(const float v[8]) {
+  int w0 = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_bf8_f32(v[4], v[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_bf8_f32(v[6], v[7], w1, true);
+  return (u32x2){(uint32_t)w0, (uint32_t)w1};
+}
+
+// MX shared exponent of a block whose largest magnitude is `amax` (fp32):
+// floor(log2(amax)) - 8 (8 = exponent of the largest e4m3fn normal, 448),
+// clamped to the E8M0 range [-127, 127]; an all-zero block takes -127.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (amax == 0.0f) return -127;
+  int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;  // amax = m * 2^k, m in [0.5, 1)
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
 // Streaming accesses: every slab, residual and output byte is touched once,
 // so loads and stores are non-temporal (they do not displace gamma in cache).
 __device__ __forceinline__ u32x4 load16(const u32x4 *p) { return __builtin_nontemporal_load(p); }
@@ -130,7 +157,8 @@ struct RowArgs {
   const u32x4 *res_in;
   u32x4 *res_out;
   u32x2 *out;  // 8 fp8 per chunk
-  float *scales;
+  float *scales;       // per-row formats: fp32 [rows]
+  uint8_t *mx_scales;  // MXFP8: E8M0 [rows, c16 / 4]
   const u32x4 *gamma;
   float eps, woff, ub;
   float cols_f;
@@ -165,7 +193,7 @@ __device__ __forceinline__ void gain2(uint32_t h, uint32_t g, float woff, float 
 // Chunk indices past the end of a ragged row are clamped to the row's last
 // chunk for the loads (an in-bounds duplicate read), and every store and
 // statistic of such a chunk is masked.
-template <int P, int VPT, bool RES_IN, bool RES_OUT>
+template <int FMT, int P, int VPT, bool RES_IN, bool RES_OUT>
 __global__ __launch_bounds__(512) void arnfp8_row_kernel(RowArgs a) {
   constexpr int G = load_group<P, VPT, RES_IN>();
   constexpr bool KEEP_HG = VPT <= 8;
@@ -246,10 +274,13 @@ __global__ __launch_bounds__(512) void arnfp8_row_kernel(RowArgs a) {
     }
 
     const float r = 1.0f / sqrtf(tot / a.cols_f + a.eps);
-    const float amax = m * r;
-    const float scale = fmaxf(fminf(amax, a.ub) / kE4m3Max, kScaleFloor);
-    const float cq = r / scale;
-    if (t == 0) a.scales[row] = scale;
+    float cq = 0.0f;
+    if constexpr (FMT != kFmtMx) {
+      const float amax = m * r;
+      const float scale = fmaxf(fminf(amax, a.ub) / fmt_max<FMT>(), fmt_floor<FMT>());
+      cq = r / scale;
+      if (t == 0) a.scales[row] = scale;
+    }
 
     constexpr int QG = KEEP_HG ? 1 : 4;  // gamma re-reads issued together
 #pragma unroll
@@ -272,11 +303,30 @@ __global__ __launch_bounds__(512) void arnfp8_row_kernel(RowArgs a) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) gain2(hk[v][w], g[k][w], a.woff, y[2 * w], y[2 * w + 1]);
         }
-        if (c <= last) {
-          float q[8];
+        float q[8];
+        if constexpr (FMT == kFmtMx) {
+          // Block of 32 = the 4 consecutive chunks of lanes 4j..4j+3 (T is a
+          // multiple of 64 and c16 of 4, so a quad is wholly valid or not).
+          float bmax = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) q[e] = fminf(fmaxf(y[e] * cq, -kE4m3Max), kE4m3Max);
-          store8(qout + c, pack_e4m3(q));
+          for (int e = 0; e < 8; ++e) {
+            y[e] = y[e] * r;
+            bmax = fmaxf(bmax, fabsf(y[e]));
+          }
+          bmax = fmaxf(bmax, __shfl_xor(bmax, 1, 64));
+          bmax = fmaxf(bmax, __shfl_xor(bmax, 2, 64));
+          const int ex = mx_shared_exp(bmax);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            q[e] = fminf(fmaxf(__builtin_amdgcn_ldexpf(y[e], -ex), -448.0f), 448.0f);
+          if (c <= last && (t & 3) == 0) a.mx_scales[row * (int64_t)(a.c16 >> 2) + (c >> 2)] = (uint8_t)(ex + 127);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            q[e] = fminf(fmaxf(y[e] * cq, -fmt_max<FMT>()), fmt_max<FMT>());
+        }
+        if (c <= last) {
+          store8(qout + c, FMT == kFmtE5m2 ? pack_e5m2(q) : pack_e4m3(q));
         }
       }
     }

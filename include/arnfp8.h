@@ -68,6 +68,7 @@ extern "C" {
 #define ARNFP8_HIP_ERROR 6    /* the launch failed (hipGetLastError)             */
 #define ARNFP8_BAD_CONFIG 7   /* an arnfp8_run_ex launch option is invalid       */
 #define ARNFP8_BAD_SHARE 8    /* ngpus < 1, or rank outside [0, ngpus)           */
+#define ARNFP8_BAD_FORMAT 9   /* unknown out_format                              */
 
 /*
  * arnfp8_run -- the fused epilogue.  For every row i and column j:
@@ -122,6 +123,38 @@ int arnfp8_run_ex(const void *const *inputs, const void *residual_in, void *resi
                   void *out_fp8, float *scales, const void *gamma, float eps,
                   float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
                   hipStream_t stream, const arnfp8_launch *opt);
+
+/* Output formats for arnfp8_run_fmt. */
+#define ARNFP8_FMT_E4M3FN 0 /* OCP e4m3fn, one fp32 scale per row (arnfp8_run)      */
+#define ARNFP8_FMT_E5M2 1   /* OCP e5m2, one fp32 scale per row                      */
+#define ARNFP8_FMT_MXFP8 2  /* OCP MXFP8: e4m3fn, one E8M0 scale per 32 values       */
+
+/*
+ * arnfp8_run_fmt -- the fused epilogue with a choice of quantised output.
+ * Per-token dynamic quantisation to E4M3FN or E5M2 and the mx (microscaling)
+ * mode are the quantisation variants of Huawei CANN aclnnAlltoAllQuantMatmul
+ * (x1QuantMode, x1QuantDtype; the mx scale shape (BS, ceil(H/64), 2)).
+ *   ARNFP8_FMT_E4M3FN  as arnfp8_run.
+ *   ARNFP8_FMT_E5M2    as arnfp8_run with the e5m2 maximum 57344 in place of
+ *                      448: scale = max(min(amax, scale_ub) / 57344,
+ *                      1 / (57344 * 512)); out_fp8 holds OCP e5m2 codes.
+ *   ARNFP8_FMT_MXFP8   no per-row scale and no scale_ub (ignored): every block
+ *                      of 32 consecutive values of a row gets the shared
+ *                      exponent e = floor(log2(max |y|)) - 8, clamped to
+ *                      [-127, 127] (-127 for an all-zero block), and its values
+ *                      are e4m3fn(clamp(y * 2^-e, -448, 448)), y = h * g * r;
+ *                      `scales` is uint8 [rows, cols / 32] holding e + 127
+ *                      (E8M0), the (rows, cols / 64, 2) layout when cols % 64
+ *                      == 0.  Requires cols % 32 == 0 (else ARNFP8_BAD_SHAPE).
+ *                      Rule: OCP Microscaling Formats v1.0 (MXFP8 E4M3).
+ * `scales` is float* for the per-row formats (4-byte aligned) and uint8_t*
+ * for MXFP8.  `opt` as for arnfp8_run_ex (may be NULL).  An unknown
+ * out_format returns ARNFP8_BAD_FORMAT.
+ */
+int arnfp8_run_fmt(const void *const *inputs, const void *residual_in, void *residual_out,
+                   void *out_fp8, void *scales, const void *gamma, float eps,
+                   float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
+                   int out_format, hipStream_t stream, const arnfp8_launch *opt);
 
 /*
  * arn_sum_bf16 -- the reduction alone: out = s as defined for arnfp8_run.
