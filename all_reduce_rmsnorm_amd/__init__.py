@@ -18,6 +18,7 @@ __all__ = [
     "arnfp8_run", "arnfp8_run_ex", "arn_sum_bf16", "arnfp8_status_string", "Launch",
     "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW", "arnfp8_stage_bytes",
     "arnfp8_run_share", "SIMD_WIDTH", "arnfp8_run_fmt", "FMT_E4M3FN", "FMT_E5M2", "FMT_MXFP8",
+    "CVT_BF16", "arnfp8_convert_f32",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +34,7 @@ STATUS = {
 FMT_E4M3FN = 0
 FMT_E5M2 = 1
 FMT_MXFP8 = 2
+CVT_BF16 = 16
 SIMD_WIDTH = 16
 
 
@@ -83,6 +85,8 @@ def library() -> ctypes.CDLL:
         L.arnfp8_run_fmt.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
                                      ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int,
                                      ctypes.c_int, vp, ctypes.POINTER(Launch)]
+        L.arnfp8_convert_f32.restype = ctypes.c_int
+        L.arnfp8_convert_f32.argtypes = [vp, vp, i64, ctypes.c_int, vp]
         L.arnfp8_stage_bytes.restype = ctypes.c_int64
         L.arnfp8_stage_bytes.argtypes = [i64, i64, ctypes.c_int]
         L.arnfp8_run_share.restype = ctypes.c_int
@@ -213,3 +217,12 @@ def arnfp8_run_fmt(inputs, residual_in, residual_out, out_fp8, scales, gamma, ep
                                   int(out_format), _stream(stream), opt)
     if st != 0:
         raise ArnFp8Error("arnfp8_run_fmt", st)
+
+
+def arnfp8_convert_f32(inp, out, fmt, n=None, stream=None) -> None:
+    """The kernels' conversion step alone: fp32 ``inp`` -> ``out`` in format
+    ``fmt`` (FMT_E4M3FN, FMT_E5M2: clamped; CVT_BF16), round to nearest even."""
+    n = int(inp.numel()) if n is None else int(n)
+    st = library().arnfp8_convert_f32(_ptr(inp), _ptr(out), n, int(fmt), _stream(stream))
+    if st != 0:
+        raise ArnFp8Error("arnfp8_convert_f32", st)

@@ -10,7 +10,11 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", "arnfp8.hip")]  # includes csrc/arnfp8_kernels.hpp
+# Translation units, compiled in parallel and linked into one library.  The
+# device code lives in csrc/arnfp8_kernels.hpp; each arnfp8_rows_*.hip holds
+# one output format's kernel instances.
+SOURCES = [os.path.join(PKG, "csrc", f) for f in
+           ("arnfp8.hip", "arnfp8_rows_e4m3.hip", "arnfp8_rows_e5m2.hip", "arnfp8_rows_mxfp8.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libarnfp8.so")
 ARCH = os.environ.get("ARNFP8_OFFLOAD_ARCH", "gfx950")
@@ -20,7 +24,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
@@ -33,12 +36,25 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into ``all_reduce_rmsnorm_amd/libarnfp8.so``."""
+    """Compile every HIP source for gfx950 and link ``all_reduce_rmsnorm_amd/libarnfp8.so``."""
+    obj_dir = os.path.join(PKG, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    procs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o")
+        cmd = [hipcc(), *HIPCC_FLAGS, "-c", f"-I{INCLUDE}", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), src))
+        objs.append(obj)
+    failed = [src for p, src in procs if p.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed for {failed}")
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", *SOURCES, "-o", tmp]
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -32,6 +32,7 @@
 
 #include "arnfp8.h"
 #include "arnfp8_kernels.hpp"
+#include "arnfp8_tables.hpp"
 
 namespace {
 
@@ -102,47 +103,11 @@ SumKernel sum_table(int P) {
   }
 }
 
-typedef void (*RowKernel)(RowArgs);
-
-template <int FMT, int P, int VPT>
-RowKernel row_kernel_res(bool res_in, bool res_out) {
-  if (res_in)
-    return res_out ? arnfp8_row_kernel<FMT, P, VPT, true, true>
-                   : arnfp8_row_kernel<FMT, P, VPT, true, false>;
-  return res_out ? arnfp8_row_kernel<FMT, P, VPT, false, true>
-                 : arnfp8_row_kernel<FMT, P, VPT, false, false>;
-}
-
-template <int FMT, int P>
-RowKernel row_kernel_vpt(int vpt, bool res_in, bool res_out) {
-  switch (vpt) {
-    case 1: return row_kernel_res<FMT, P, 1>(res_in, res_out);
-    case 2: return row_kernel_res<FMT, P, 2>(res_in, res_out);
-    case 4: return row_kernel_res<FMT, P, 4>(res_in, res_out);
-    case 8: return row_kernel_res<FMT, P, 8>(res_in, res_out);
-    default: return row_kernel_res<FMT, P, 16>(res_in, res_out);
-  }
-}
-
-template <int FMT>
-RowKernel row_kernel_p(int P, int vpt, bool res_in, bool res_out) {
-  switch (P) {
-    case 1: return row_kernel_vpt<FMT, 1>(vpt, res_in, res_out);
-    case 2: return row_kernel_vpt<FMT, 2>(vpt, res_in, res_out);
-    case 3: return row_kernel_vpt<FMT, 3>(vpt, res_in, res_out);
-    case 4: return row_kernel_vpt<FMT, 4>(vpt, res_in, res_out);
-    case 5: return row_kernel_vpt<FMT, 5>(vpt, res_in, res_out);
-    case 6: return row_kernel_vpt<FMT, 6>(vpt, res_in, res_out);
-    case 7: return row_kernel_vpt<FMT, 7>(vpt, res_in, res_out);
-    default: return row_kernel_vpt<FMT, 8>(vpt, res_in, res_out);
-  }
-}
-
 RowKernel row_table(int fmt, int P, int vpt, bool res_in, bool res_out) {
   switch (fmt) {
-    case ARNFP8_FMT_E5M2: return row_kernel_p<kFmtE5m2>(P, vpt, res_in, res_out);
-    case ARNFP8_FMT_MXFP8: return row_kernel_p<kFmtMx>(P, vpt, res_in, res_out);
-    default: return row_kernel_p<kFmtE4m3>(P, vpt, res_in, res_out);
+    case ARNFP8_FMT_E5M2: return row_table_e5m2(P, vpt, res_in, res_out);
+    case ARNFP8_FMT_MXFP8: return row_table_mxfp8(P, vpt, res_in, res_out);
+    default: return row_table_e4m3(P, vpt, res_in, res_out);
   }
 }
 
@@ -153,15 +118,17 @@ struct RowConfig {
 };
 
 // Smallest chunks-per-lane (1, 2, 4, 8, 16) that fits the row in at most 512
-// lanes; lanes rounded up to whole waves.
+// lanes.  With one chunk per lane the lanes are rounded up to whole waves;
+// with more, all 512 lanes are used (measured on MI355X: 512 lanes x 2 chunks
+// beat 448 x 2 for a 7168-wide row at every batch size, and 1024 x 1).
 RowConfig pick_row_config(int64_t rows, int c16) {
   static const int vpts[5] = {1, 2, 4, 8, 16};
-  RowConfig cfg{64, 16, 1};
+  RowConfig cfg{512, 16, 1};
   for (int i = 0; i < 5; ++i) {
     const int lanes = (c16 + vpts[i] - 1) / vpts[i];
     if (lanes <= 512) {
       cfg.vpt = vpts[i];
-      cfg.threads = ((lanes + 63) / 64) * 64;
+      cfg.threads = vpts[i] == 1 ? ((lanes + 63) / 64) * 64 : 512;
       break;
     }
   }
@@ -232,7 +199,7 @@ int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfi
     return ARNFP8_BAD_CONFIG;
   if (opt->threads < 0 || opt->vpt < 0 || opt->grid < 0) return ARNFP8_BAD_CONFIG;
   if (opt->threads) {
-    if (opt->threads % 64 != 0 || opt->threads > 512) return ARNFP8_BAD_CONFIG;
+    if (opt->threads % 64 != 0 || opt->threads > 1024) return ARNFP8_BAD_CONFIG;
     cfg->threads = opt->threads;
     if (!opt->vpt) {  // the smallest chunks-per-lane that covers the row
       static const int vpts[5] = {1, 2, 4, 8, 16};
@@ -247,8 +214,9 @@ int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfi
       return ARNFP8_BAD_CONFIG;
     cfg->vpt = opt->vpt;
     if (!opt->threads) cfg->threads = ((c16 + cfg->vpt - 1) / cfg->vpt + 63) / 64 * 64;
-    if (cfg->threads > 512) return ARNFP8_BAD_CONFIG;
   }
+  // One chunk per lane allows up to 1024 lanes; more chunks per lane, 512.
+  if (cfg->threads > (cfg->vpt == 1 ? 1024 : 512)) return ARNFP8_BAD_CONFIG;
   if ((int64_t)cfg->threads * cfg->vpt < c16) return ARNFP8_BAD_CONFIG;
   if (opt->grid) cfg->grid = opt->grid;
   return ARNFP8_OK;
@@ -389,6 +357,34 @@ extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_
   hipLaunchKernelGGL(row_table(ARNFP8_FMT_E4M3FN, P, cfg.vpt, residual_in != nullptr,
                                residual_out != nullptr),
                      dim3(cfg.grid), dim3(cfg.threads), 0, stream, a);
+  return launch_status();
+}
+
+extern "C" int arnfp8_convert_f32(const float *in, void *out, int64_t n, int format,
+                                  hipStream_t stream) {
+  if (format != ARNFP8_FMT_E4M3FN && format != ARNFP8_FMT_E5M2 && format != ARNFP8_CVT_BF16)
+    return ARNFP8_BAD_FORMAT;
+  if (n < 0 || n % 8 != 0 || n > INT64_MAX / 4) return ARNFP8_BAD_SHAPE;
+  if (n == 0) return ARNFP8_OK;
+  if (in == nullptr || out == nullptr) return ARNFP8_NULL_POINTER;
+  if (!aligned(in, 16) || !aligned(out, 16)) return ARNFP8_MISALIGNED;
+  const uintptr_t out_bytes = (uintptr_t)n * (format == ARNFP8_CVT_BF16 ? 2 : 1);
+  if (overlaps(Range{(uintptr_t)in, (uintptr_t)in + 4 * (uintptr_t)n},
+               Range{(uintptr_t)out, (uintptr_t)out + out_bytes}))
+    return ARNFP8_ALIAS;
+  const int64_t n8 = n / 8;
+  int64_t blocks = (n8 + 255) / 256;
+  if (blocks > (int64_t)device_cus() * 8) blocks = (int64_t)device_cus() * 8;
+  const u32x4 *src = (const u32x4 *)in;
+  if (format == ARNFP8_FMT_E4M3FN)
+    hipLaunchKernelGGL(cvt_kernel<ARNFP8_FMT_E4M3FN>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       src, out, n8);
+  else if (format == ARNFP8_FMT_E5M2)
+    hipLaunchKernelGGL(cvt_kernel<ARNFP8_FMT_E5M2>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       src, out, n8);
+  else
+    hipLaunchKernelGGL(cvt_kernel<ARNFP8_CVT_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       src, out, n8);
   return launch_status();
 }
 

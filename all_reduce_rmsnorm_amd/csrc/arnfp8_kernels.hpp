@@ -152,6 +152,35 @@ __global__ __launch_bounds__(256) void arn_sum_kernel(Slabs in, u32x4 *__restric
   }
 }
 
+// The kernels' conversion steps on their own: 8 fp32 per lane per step ->
+// e4m3fn (clamped to +-448), e5m2 (clamped to +-57344) or bf16 (round to
+// nearest even, unclamped), exactly as the fused kernel converts.
+template <int FMT>
+__global__ __launch_bounds__(256) void cvt_kernel(const u32x4 *__restrict__ in,
+                                                  void *__restrict__ out, int64_t n8) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const u32x4 a = in[2 * i], b = in[2 * i + 1];
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = __uint_as_float(a[k]);
+      v[4 + k] = __uint_as_float(b[k]);
+    }
+    if constexpr (FMT == ARNFP8_CVT_BF16) {
+      u32x4 w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = pack_bf16(v[2 * k], v[2 * k + 1]);
+      ((u32x4 *)out)[i] = w;
+    } else {
+      constexpr float lim = FMT == ARNFP8_FMT_E5M2 ? 57344.0f : 448.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = fminf(fmaxf(v[k], -lim), lim);
+      ((u32x2 *)out)[i] = FMT == ARNFP8_FMT_E5M2 ? pack_e5m2(v) : pack_e4m3(v);
+    }
+  }
+}
+
 struct RowArgs {
   Slabs in;
   const u32x4 *res_in;
@@ -194,10 +223,10 @@ __device__ __forceinline__ void gain2(uint32_t h, uint32_t g, float woff, float 
 // chunk for the loads (an in-bounds duplicate read), and every store and
 // statistic of such a chunk is masked.
 template <int FMT, int P, int VPT, bool RES_IN, bool RES_OUT>
-__global__ __launch_bounds__(512) void arnfp8_row_kernel(RowArgs a) {
+__global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowArgs a) {
   constexpr int G = load_group<P, VPT, RES_IN>();
   constexpr bool KEEP_HG = VPT <= 8;
-  __shared__ float red[2][8][2];  // [row parity][wave][sum h^2, max |h g|]
+  __shared__ float red[2][16][2];  // [row parity][wave][sum h^2, max |h g|]
   const int t = threadIdx.x;
   const int T = blockDim.x;
   const int wave = t >> 6;

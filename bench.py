@@ -44,6 +44,7 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "arnfp8_row_kernel_prefill_p8_8192x
 # The device code and the flags it is built with: the committed HBM-counter
 # summary applies only while these are unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_kernels.hpp"),
+                  os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_tables.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
 
 
@@ -403,6 +404,17 @@ def main():
             "fused_speedup": round(un_ms / ms_per_step, 3),
         }
         log(f"bench: unfused two-launch chain {un_ms * 1e3:.2f} us/step")
+        # The other output formats on the same workload and bytes (the MX
+        # block scales replace the per-row scales: rows * cols / 32 bytes).
+        fmt_out = {}
+        mx_scales = torch.empty((w.rows, w.cols // 32), dtype=torch.uint8, device=dev)
+        for name, fmt, sc in (("e5m2", arn.FMT_E5M2, d["scales"]), ("mxfp8", arn.FMT_MXFP8, mx_scales)):
+            _, f_k = time_steps(torch, lambda: arn.arnfp8_run_fmt(
+                d["inputs"], d["residual"], d["res_out"], d["out"], sc, d["gamma"], w.eps,
+                w.weight_offset, w.scale_ub, out_format=fmt), max(10, args.steps // 2), 3)
+            fmt_out[f"{name}_us_per_call"] = round(f_k * 1e3, 2)
+        result["formats"] = fmt_out
+        del mx_scales
         # One rank's share of the two-stage layout (8 ranks): the single-GPU
         # half of the large-payload path, at its real shape.
         ngpus = 8

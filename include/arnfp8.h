@@ -105,7 +105,8 @@ int arnfp8_run(const void *const *inputs, const void *residual_in, void *residua
 /* Launch options for arnfp8_run_ex.  Zero in any field means "automatic". */
 typedef struct arnfp8_launch {
   int variant; /* ARNFP8_VARIANT_*                                               */
-  int threads; /* lanes per workgroup: a multiple of 64 in [64, 512]           */
+  int threads; /* lanes per workgroup: a multiple of 64 in [64, 512], or up to
+                  1024 with one chunk per lane (vpt 1)                          */
   int vpt;     /* 16-byte chunks per lane: 1, 2, 4, 8 or 16                    */
   int grid;    /* workgroups; rows are walked grid-stride (>= 1)               */
 } arnfp8_launch;
@@ -197,6 +198,19 @@ int arnfp8_run_share(const void *const *inputs, const void *residual_in, void *r
                      void *staging, const void *gamma, float eps, float weight_offset,
                      float scale_ub, int64_t rows, int64_t cols, int P, int ngpus, int rank,
                      hipStream_t stream);
+
+/*
+ * arnfp8_convert_f32 -- the kernels' number-format conversion step on its own
+ * (for checking the hardware conversion instructions exhaustively).
+ *   ARNFP8_FMT_E4M3FN  out = e4m3fn(clamp(in, -448, 448)),     1 byte each
+ *   ARNFP8_FMT_E5M2    out = e5m2(clamp(in, -57344, 57344)),   1 byte each
+ *   ARNFP8_CVT_BF16    out = bf16(in),                          2 bytes each
+ * all round to nearest even.  in: device fp32 [n]; out: device [n] of the
+ * format; n % 8 == 0; both 16-byte aligned and not overlapping.  NaN inputs
+ * give unspecified codes.  Returns ARNFP8_BAD_FORMAT for any other format.
+ */
+#define ARNFP8_CVT_BF16 16
+int arnfp8_convert_f32(const float *in, void *out, int64_t n, int format, hipStream_t stream);
 
 /* Human-readable text for a status code (a static string; never NULL). */
 const char *arnfp8_status_string(int status);

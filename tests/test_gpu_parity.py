@@ -340,7 +340,8 @@ def test_unfused_two_launch_chain_is_bitwise_equal(arn, synth):
     assert torch.equal(fused[1], unfused[1]) and torch.equal(fused[2], unfused[2])
 
 
-@pytest.mark.parametrize("launch", [dict(threads=64, vpt=16), dict(threads=128, vpt=8),
+@pytest.mark.parametrize("launch", [dict(threads=960, vpt=1), dict(threads=1024),
+                                    dict(threads=64, vpt=16), dict(threads=128, vpt=8),
                                     dict(threads=256, vpt=4), dict(threads=512, vpt=2),
                                     dict(threads=448, vpt=4, grid=7), dict(threads=320, vpt=4, grid=1)])
 def test_every_launch_shape_matches_the_oracle(arn, orc, launch):
@@ -364,7 +365,8 @@ def test_bad_launch_options_rejected(arn):
     out = torch.empty((4, 1024), dtype=torch.float8_e4m3fn, device=DEV)
     s = torch.empty((4,), dtype=torch.float32, device=DEV)
     g = torch.ones((1024,), dtype=torch.bfloat16, device=DEV)
-    for bad in (dict(threads=96), dict(threads=1024), dict(vpt=3), dict(threads=64, vpt=1),
+    for bad in (dict(threads=96), dict(threads=1024, vpt=2), dict(threads=1088), dict(vpt=3),
+                dict(threads=64, vpt=1),
                 dict(grid=-1), dict(variant=9)):
         with pytest.raises(arn.ArnFp8Error) as e:
             arn.arnfp8_run_ex([x], None, None, out, s, g, 1e-6, 0.0, 1.0, launch=bad)
