@@ -118,17 +118,20 @@ struct RowConfig {
 };
 
 // Smallest chunks-per-lane (1, 2, 4, 8, 16) that fits the row in at most 512
-// lanes.  With one chunk per lane the lanes are rounded up to whole waves;
-// with more, all 512 lanes are used (measured on MI355X: 512 lanes x 2 chunks
-// beat 448 x 2 for a 7168-wide row at every batch size, and 1024 x 1).
+// lanes.  Lanes are rounded up to whole waves, except that batches smaller
+// than four rows per CU use all 512 lanes when a lane holds two or more
+// chunks.  Measured on MI355X for 7168-wide rows: 512 x 2 beats 448 x 2 by
+// ~3 % at 1-128 rows (and 1024 x 1 everywhere); 448 x 2 beats 512 x 2 by
+// ~1 % at 8192 rows.
 RowConfig pick_row_config(int64_t rows, int c16) {
   static const int vpts[5] = {1, 2, 4, 8, 16};
+  const bool small_batch = rows < 1024 || rows < 4 * (int64_t)device_cus();
   RowConfig cfg{512, 16, 1};
   for (int i = 0; i < 5; ++i) {
     const int lanes = (c16 + vpts[i] - 1) / vpts[i];
     if (lanes <= 512) {
       cfg.vpt = vpts[i];
-      cfg.threads = vpts[i] == 1 ? ((lanes + 63) / 64) * 64 : 512;
+      cfg.threads = (vpts[i] > 1 && small_batch) ? 512 : ((lanes + 63) / 64) * 64;
       break;
     }
   }
@@ -264,13 +267,13 @@ extern "C" int arnfp8_run_fmt(const void *const *inputs, const void *residual_in
       out_format != ARNFP8_FMT_MXFP8)
     return ARNFP8_BAD_FORMAT;
   if (out_format == ARNFP8_FMT_MXFP8 && cols % 32 != 0) return ARNFP8_BAD_SHAPE;
-  RowConfig cfg;
-  st = resolve_row_config(opt, rows, (int)(cols / 8), &cfg);
-  if (st != ARNFP8_OK) return st;
   if (rows == 0) return ARNFP8_OK;
   RowArgs a;
   st = prepare_fused(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
                      weight_offset, scale_ub, rows, cols, P, &a, out_format);
+  if (st != ARNFP8_OK) return st;
+  RowConfig cfg;  // after validation: the automatic choice queries the device
+  st = resolve_row_config(opt, rows, (int)(cols / 8), &cfg);
   if (st != ARNFP8_OK) return st;
   hipLaunchKernelGGL(row_table(out_format, P, cfg.vpt, residual_in != nullptr,
                                residual_out != nullptr),
@@ -347,12 +350,12 @@ extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_
     return ARNFP8_OK;
   }
 
-  RowConfig cfg;
-  st = resolve_row_config(nullptr, count, (int)(cols / 8), &cfg);
-  if (st != ARNFP8_OK) return st;
   RowArgs a;
   st = prepare_fused(shifted, rin, rout, out, scales, gamma, eps, weight_offset, scale_ub, count,
                      cols, P, &a);
+  if (st != ARNFP8_OK) return st;
+  RowConfig cfg;
+  st = resolve_row_config(nullptr, count, (int)(cols / 8), &cfg);
   if (st != ARNFP8_OK) return st;
   hipLaunchKernelGGL(row_table(ARNFP8_FMT_E4M3FN, P, cfg.vpt, residual_in != nullptr,
                                residual_out != nullptr),

@@ -199,3 +199,20 @@ def test_share_validation_codes(L):
     assert share(4, 1, cols=12) == BAD_SHAPE
     # an empty share validates and returns OK without launching
     assert share(8, 7, rows=5) == OK
+
+
+def test_bad_launch_options_rejected_without_device(L):
+    import all_reduce_rmsnorm_amd as arn
+
+    x0, x1 = BASE, BASE + 10 * MB
+    for bad in (arn.Launch(threads=96), arn.Launch(threads=1024, vpt=2), arn.Launch(vpt=3),
+                arn.Launch(threads=64, vpt=1), arn.Launch(grid=-1), arn.Launch(variant=9)):
+        st = L.arnfp8_run_ex(_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 200 * MB,
+                             BASE + 300 * MB, 1e-6, 0.0, 1.0, 4, 1024, 2, None, ctypes.byref(bad))
+        assert st == 7, (bad.threads, bad.vpt, bad.grid, bad.variant)
+    st = L.arnfp8_run_fmt(_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 200 * MB,
+                          BASE + 300 * MB, 1e-6, 0.0, 1.0, 4, 1024, 2, 5, None, None)
+    assert st == 9
+    st = L.arnfp8_run_fmt(_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 200 * MB,
+                          BASE + 300 * MB, 1e-6, 0.0, 1.0, 4, 1000, 2, 2, None, None)
+    assert st == BAD_SHAPE  # MXFP8 needs cols % 32 == 0
