@@ -419,3 +419,73 @@ def test_two_stage_share_and_staging_layout(arn, orc, ngpus):
         full_q = full[0].view(torch.uint8).cpu().numpy()[first:first + count]
         assert np.array_equal(data_g[:count], full_q)
         assert np.array_equal(sc_g, full[1].cpu().numpy()[first:first + count])
+
+
+def test_slabs_larger_than_4GiB(arn, orc):
+    """64-bit offsets: P = 2 slabs of 4.3 GiB each (rows x cols x 2 bytes > 2^32);
+    the oracle checks rows past the 4 GiB mark, and the sum kernel the same."""
+    rows, cols = 1_100_000, 2048
+    print(f"[fused] >4GiB slabs rows={rows} cols={cols}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(99)
+    xs = [torch.randn((rows, cols), generator=g, device=DEV, dtype=torch.bfloat16) for _ in range(2)]
+    gamma = torch.ones((cols,), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    scales = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    res_out = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    arn.arnfp8_run(xs, None, res_out, out, scales, gamma, 1e-6, 0.0, 1200.0)
+    torch.cuda.synchronize()
+    pick = torch.tensor([0, 1048575, 1048576, 1048577, rows - 2, rows - 1], device=DEV)
+    xs_h = [x.index_select(0, pick).cpu() for x in xs]
+    q, s, h = orc.arnfp8([_bits(x) for x in xs_h], _bits(gamma.cpu()), 1e-6, 0.0, 1200.0)
+    assert_bits_equal(_bits(res_out.index_select(0, pick)), h, "residual_out")
+    assert_scales_close(scales.index_select(0, pick).cpu().numpy(), s)
+    assert_fp8_close(out.index_select(0, pick).cpu().numpy(), q, min_exact=0.99)
+    del out, scales
+    sum_out = res_out
+    sum_out.fill_(0)
+    arn.arn_sum_bf16(xs, sum_out)
+    torch.cuda.synchronize()
+    assert_bits_equal(_bits(sum_out.index_select(0, pick)), h, "sum")
+
+
+def test_graph_replay_of_share_and_formats(arn, synth):
+    """The share and the e5m2 / MXFP8 entry points captured in one graph:
+    every replay equals the eager result bitwise."""
+    w = synth.WORKLOADS["decode_p4_32x7168"]
+    d = synth.make_inputs(w, device=DEV)
+    rows, cols = w.rows, w.cols
+    stg = torch.zeros((arn.arnfp8_stage_bytes(rows, cols, 4),), dtype=torch.uint8, device=DEV)
+    q5 = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    s5 = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    qm = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    sm = torch.empty((rows, cols // 32), dtype=torch.uint8, device=DEV)
+    ro = torch.zeros((rows, cols), dtype=torch.bfloat16, device=DEV)  # rows outside the share stay 0
+
+    def calls():
+        arn.arnfp8_run_share(d["inputs"], d["residual"], ro, stg, d["gamma"], w.eps, 0.0, 1200.0,
+                             ngpus=4, rank=2)
+        arn.arnfp8_run_fmt(d["inputs"], d["residual"], None, q5, s5, d["gamma"], w.eps, 0.0,
+                           1200.0, out_format=arn.FMT_E5M2)
+        arn.arnfp8_run_fmt(d["inputs"], d["residual"], None, qm, sm, d["gamma"], w.eps, 0.0,
+                           0.0, out_format=arn.FMT_MXFP8)
+
+    calls()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (stg, q5, s5, qm, sm, ro)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for k in range(3):
+        for t in (stg, q5, qm, sm):
+            t.fill_(0x5A)
+        s5.fill_(-1.0)
+        ro.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((stg, q5, s5, qm, sm, ro), eager):
+            assert torch.equal(a, b), k
