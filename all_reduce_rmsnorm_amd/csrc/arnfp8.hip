@@ -1,34 +1,19 @@
-// arnfp8.hip -- gfx950 (CDNA4) kernels and the C ABI of the fused all-reduce
-// epilogue: rank-order fp32 sum of P bf16 slabs rounded once to bf16, optional
-// residual add and write-back, RMSNorm with gamma + weight_offset, and per-row
-// dynamic fp8 e4m3fn quantisation, in one launch.
+// arnfp8.hip -- the C ABI of the fused all-reduce epilogue library for gfx950:
+// argument validation (on the host, before any device query or launch),
+// the automatic launch shape, and the launches.  The device code is in
+// arnfp8_kernels.hpp; the row kernel's instances are built per output format
+// in arnfp8_rows_*.hip.
 //
 // Sources: Modular Mojo API docs "allreduce_rmsnorm_fp8" (function summary,
-// Args); b12x PR #283 "PCIeTwoShotBF16" (PR description); TensorRT-LLM PR
-// #19836 (Description, RESIDUAL_RMS_NORM); tt-metal rmsnorm_2d.py
-// (add_unit_offset).
-//
-// Design (HBM-bound, not a contraction, so no MFMA):
-//  * One workgroup owns a row at a time; a row is cut into 16-byte chunks of
-//    8 bf16 and lane t of a T-lane workgroup owns chunks t, t + T, ...  Every
-//    global access is a 16-byte vector per lane, so a wave moves 1 KiB per
-//    load instruction, fully coalesced.
-//  * For each chunk the P slab loads (and the residual load) are issued
-//    together, then summed in fp32 in rank order and rounded once with the
-//    gfx950 packed bf16 conversion (round to nearest even).
-//  * The row stays in registers as packed bf16 between the statistics pass and
-//    the quantisation pass: the only global traffic is the algorithmic one.
-//  * (sum h^2, max |h g|) are reduced across the wave with butterfly lane
-//    exchanges and across waves through LDS with a single barrier per row;
-//    the LDS slot alternates with the row parity so consecutive rows of a
-//    grid-stride loop need no second barrier.
-//  * fp8 values come from the gfx950 packed fp32 -> OCP e4m3fn conversion,
-//    after an explicit clamp to +-448, so the conversion never overflows.
-//  * Every lane reaches every barrier; chunk guards only guard data accesses.
+// Args; the 2-stage signal buffer sizing); b12x PR #283 "PCIeTwoShotBF16" (PR
+// description; the validation the review asks for: alignment, output
+// tensors checked before any launch); Huawei CANN aclnnAlltoAllQuantMatmul
+// (output formats).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <string.h>
+
+#include <atomic>
 
 #include "arnfp8.h"
 #include "arnfp8_kernels.hpp"
@@ -64,21 +49,28 @@ int check_inputs(const void *const *inputs, int P) {
   return ARNFP8_OK;
 }
 
-int launch_status() {
-  return hipGetLastError() == hipSuccess ? ARNFP8_OK : ARNFP8_HIP_ERROR;
+// Launches `kernel` with its arguments passed by value; the status is that of
+// this launch alone (not an earlier error left in the thread's HIP state).
+template <typename... Args>
+int launch(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  void *argv[] = {(void *)&args...};
+  return hipLaunchKernel((const void *)kernel, grid, block, argv, 0, stream) == hipSuccess
+             ? ARNFP8_OK
+             : ARNFP8_HIP_ERROR;
 }
 
+// Compute units of the current device (queried once per device).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // ---- launch tables: one entry per template instance ----
@@ -125,7 +117,7 @@ struct RowConfig {
 // ~1 % at 8192 rows.
 RowConfig pick_row_config(int64_t rows, int c16) {
   static const int vpts[5] = {1, 2, 4, 8, 16};
-  const bool small_batch = rows < 1024 || rows < 4 * (int64_t)device_cus();
+  const bool small_batch = rows < 4 * (int64_t)device_cus();
   RowConfig cfg{512, 16, 1};
   for (int i = 0; i < 5; ++i) {
     const int lanes = (c16 + vpts[i] - 1) / vpts[i];
@@ -194,34 +186,43 @@ int prepare_fused(const void *const *inputs, const void *residual_in, void *resi
   return ARNFP8_OK;
 }
 
-// Resolves the launch options against the automatic choice.
+// Resolves the launch options against the automatic choice.  The options are
+// checked first; the device is queried only when lanes and chunks per lane
+// are both left automatic.
 int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfig *cfg) {
-  *cfg = pick_row_config(rows, c16);
-  if (opt == nullptr) return ARNFP8_OK;
+  static const int vpts[5] = {1, 2, 4, 8, 16};
+  if (opt == nullptr) {
+    *cfg = pick_row_config(rows, c16);
+    return ARNFP8_OK;
+  }
   if (opt->variant != ARNFP8_VARIANT_AUTO && opt->variant != ARNFP8_VARIANT_ROW)
     return ARNFP8_BAD_CONFIG;
   if (opt->threads < 0 || opt->vpt < 0 || opt->grid < 0) return ARNFP8_BAD_CONFIG;
-  if (opt->threads) {
-    if (opt->threads % 64 != 0 || opt->threads > 1024) return ARNFP8_BAD_CONFIG;
+  if (opt->threads && (opt->threads % 64 != 0 || opt->threads > 1024)) return ARNFP8_BAD_CONFIG;
+  if (opt->vpt && opt->vpt != 1 && opt->vpt != 2 && opt->vpt != 4 && opt->vpt != 8 &&
+      opt->vpt != 16)
+    return ARNFP8_BAD_CONFIG;
+  if (opt->threads && opt->vpt) {
     cfg->threads = opt->threads;
-    if (!opt->vpt) {  // the smallest chunks-per-lane that covers the row
-      static const int vpts[5] = {1, 2, 4, 8, 16};
-      cfg->vpt = 0;
-      for (int i = 0; i < 5 && !cfg->vpt; ++i)
-        if ((int64_t)vpts[i] * cfg->threads >= c16) cfg->vpt = vpts[i];
-      if (!cfg->vpt) return ARNFP8_BAD_CONFIG;
-    }
-  }
-  if (opt->vpt) {
-    if (opt->vpt != 1 && opt->vpt != 2 && opt->vpt != 4 && opt->vpt != 8 && opt->vpt != 16)
-      return ARNFP8_BAD_CONFIG;
     cfg->vpt = opt->vpt;
-    if (!opt->threads) cfg->threads = ((c16 + cfg->vpt - 1) / cfg->vpt + 63) / 64 * 64;
+  } else if (opt->threads) {  // the smallest chunks-per-lane that covers the row
+    cfg->threads = opt->threads;
+    cfg->vpt = 0;
+    for (int i = 0; i < 5 && !cfg->vpt; ++i)
+      if ((int64_t)vpts[i] * cfg->threads >= c16) cfg->vpt = vpts[i];
+    if (!cfg->vpt) return ARNFP8_BAD_CONFIG;
+  } else if (opt->vpt) {  // the lanes that cover the row, in whole waves
+    cfg->vpt = opt->vpt;
+    cfg->threads = ((c16 + cfg->vpt - 1) / cfg->vpt + 63) / 64 * 64;
+  } else {
+    *cfg = pick_row_config(rows, c16);
   }
   // One chunk per lane allows up to 1024 lanes; more chunks per lane, 512.
   if (cfg->threads > (cfg->vpt == 1 ? 1024 : 512)) return ARNFP8_BAD_CONFIG;
   if ((int64_t)cfg->threads * cfg->vpt < c16) return ARNFP8_BAD_CONFIG;
-  if (opt->grid) cfg->grid = opt->grid;
+  cfg->grid = opt->grid ? opt->grid : (int)(rows < 65536 ? rows : 65536);
+  // A dispatch counts its work-items in 32 bits.
+  if ((int64_t)cfg->grid * cfg->threads > (int64_t)UINT32_MAX) return ARNFP8_BAD_CONFIG;
   return ARNFP8_OK;
 }
 
@@ -251,9 +252,7 @@ extern "C" int arn_sum_bf16(const void *const *inputs, void *out, int64_t rows, 
   int64_t blocks = (n16 + threads * U - 1) / (threads * U);
   const int64_t cap = (int64_t)device_cus() * 16;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(sum_table(P), dim3((unsigned)blocks), dim3(threads), 0, stream, s, (u32x4 *)out,
-                     n16);
-  return launch_status();
+  return launch(sum_table(P), dim3((unsigned)blocks), dim3(threads), stream, s, (u32x4 *)out, n16);
 }
 
 extern "C" int arnfp8_run_fmt(const void *const *inputs, const void *residual_in,
@@ -275,10 +274,8 @@ extern "C" int arnfp8_run_fmt(const void *const *inputs, const void *residual_in
   RowConfig cfg;  // after validation: the automatic choice queries the device
   st = resolve_row_config(opt, rows, (int)(cols / 8), &cfg);
   if (st != ARNFP8_OK) return st;
-  hipLaunchKernelGGL(row_table(out_format, P, cfg.vpt, residual_in != nullptr,
-                               residual_out != nullptr),
-                     dim3(cfg.grid), dim3(cfg.threads), 0, stream, a);
-  return launch_status();
+  return launch(row_table(out_format, P, cfg.vpt, residual_in != nullptr, residual_out != nullptr),
+                dim3(cfg.grid), dim3(cfg.threads), stream, a);
 }
 
 extern "C" int arnfp8_run_ex(const void *const *inputs, const void *residual_in,
@@ -357,10 +354,9 @@ extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_
   RowConfig cfg;
   st = resolve_row_config(nullptr, count, (int)(cols / 8), &cfg);
   if (st != ARNFP8_OK) return st;
-  hipLaunchKernelGGL(row_table(ARNFP8_FMT_E4M3FN, P, cfg.vpt, residual_in != nullptr,
-                               residual_out != nullptr),
-                     dim3(cfg.grid), dim3(cfg.threads), 0, stream, a);
-  return launch_status();
+  return launch(row_table(ARNFP8_FMT_E4M3FN, P, cfg.vpt, residual_in != nullptr,
+                          residual_out != nullptr),
+                dim3(cfg.grid), dim3(cfg.threads), stream, a);
 }
 
 extern "C" int arnfp8_convert_f32(const float *in, void *out, int64_t n, int format,
@@ -379,16 +375,12 @@ extern "C" int arnfp8_convert_f32(const float *in, void *out, int64_t n, int for
   int64_t blocks = (n8 + 255) / 256;
   if (blocks > (int64_t)device_cus() * 8) blocks = (int64_t)device_cus() * 8;
   const u32x4 *src = (const u32x4 *)in;
+  const dim3 grid((unsigned)blocks), block(256);
   if (format == ARNFP8_FMT_E4M3FN)
-    hipLaunchKernelGGL(cvt_kernel<ARNFP8_FMT_E4M3FN>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       src, out, n8);
-  else if (format == ARNFP8_FMT_E5M2)
-    hipLaunchKernelGGL(cvt_kernel<ARNFP8_FMT_E5M2>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       src, out, n8);
-  else
-    hipLaunchKernelGGL(cvt_kernel<ARNFP8_CVT_BF16>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       src, out, n8);
-  return launch_status();
+    return launch(cvt_kernel<ARNFP8_FMT_E4M3FN>, grid, block, stream, src, out, n8);
+  if (format == ARNFP8_FMT_E5M2)
+    return launch(cvt_kernel<ARNFP8_FMT_E5M2>, grid, block, stream, src, out, n8);
+  return launch(cvt_kernel<ARNFP8_CVT_BF16>, grid, block, stream, src, out, n8);
 }
 
 extern "C" const char *arnfp8_status_string(int status) {
@@ -399,7 +391,7 @@ extern "C" const char *arnfp8_status_string(int status) {
     case ARNFP8_BAD_SHAPE: return "bad shape (rows >= 0, 0 < cols <= 65536, cols % 8 == 0)";
     case ARNFP8_BAD_P: return "P must be in [1, 8]";
     case ARNFP8_ALIAS: return "an output overlaps an input or another output";
-    case ARNFP8_HIP_ERROR: return "HIP launch error";
+    case ARNFP8_HIP_ERROR: return "the kernel launch failed";
     case ARNFP8_BAD_CONFIG: return "invalid launch configuration";
     case ARNFP8_BAD_SHARE: return "bad share: ngpus must be >= 1 and 0 <= rank < ngpus";
     case ARNFP8_BAD_FORMAT: return "unknown output format";

@@ -1,11 +1,36 @@
 // arnfp8_kernels.hpp -- gfx950 (CDNA4) device code of the fused all-reduce
-// epilogue: the rank-order sum kernel and the fused row kernel.  Included by
-// arnfp8.hip (the C ABI); nothing here is visible outside that translation unit.
+// epilogue: the rank-order sum kernel, the fused row kernel and the
+// conversion kernel.  Included by the C ABI (arnfp8.hip) and by the
+// per-format instance units (arnfp8_rows_*.hip).
 //
 // Sources: Modular Mojo API docs "allreduce_rmsnorm_fp8" (function summary,
 // Args); b12x PR #283 "PCIeTwoShotBF16" (PR description); TensorRT-LLM PR
 // #19836 (Description, RESIDUAL_RMS_NORM); tt-metal rmsnorm_2d.py
-// (add_unit_offset).
+// (add_unit_offset); Huawei CANN aclnnAlltoAllQuantMatmul (E5M2 and mx
+// quantisation).
+//
+// Design (the path is HBM-bound and not a contraction, so no MFMA):
+//  * A workgroup owns a row at a time (rows walked grid-stride).  A row is cut
+//    into 16-byte chunks of 8 bf16; lane t of a T-lane workgroup owns chunks
+//    t, t + T, ...  Every global access is a 16-byte vector per lane, so a
+//    wave moves 1 KiB per instruction, fully coalesced.
+//  * All P slab loads, the residual load and the gamma load of a lane's chunks
+//    are issued before any is consumed (within a register budget); indices
+//    past a ragged row's end are clamped for the loads and masked for stores
+//    and statistics.  Slabs and residual are streamed non-temporally.
+//  * The sum is accumulated in fp32 in rank order and rounded once with the
+//    packed bf16 conversion (round to nearest even); the residual add is
+//    rounded the same way.
+//  * fl32(h * g) stays in registers between the statistics pass and the
+//    quantisation pass: the only global traffic is the algorithmic one.
+//  * (sum h^2, max |h g|) are reduced across the wave with butterfly lane
+//    exchanges and across waves through LDS with one barrier per row; the LDS
+//    slot alternates with the row parity so consecutive rows need no second
+//    barrier.
+//  * fp8 values come from the packed OCP e4m3fn / e5m2 conversions after an
+//    explicit clamp, so a conversion never overflows.
+//  * Every lane reaches every barrier and every lane exchange; guards only
+//    guard data accesses.
 #pragma once
 
 #include <hip/hip_runtime.h>
