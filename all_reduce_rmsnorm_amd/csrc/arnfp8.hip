@@ -77,21 +77,17 @@ int device_cus() {
 
 typedef void (*SumKernel)(Slabs, u32x4 *, int64_t);
 
-template <int P>
-SumKernel sum_kernel_for() {
-  return arn_sum_kernel<P, 2>;
-}
-
-SumKernel sum_table(int P) {
+template <int U>
+SumKernel sum_kernel_p(int P) {
   switch (P) {
-    case 1: return sum_kernel_for<1>();
-    case 2: return sum_kernel_for<2>();
-    case 3: return sum_kernel_for<3>();
-    case 4: return sum_kernel_for<4>();
-    case 5: return sum_kernel_for<5>();
-    case 6: return sum_kernel_for<6>();
-    case 7: return sum_kernel_for<7>();
-    default: return sum_kernel_for<8>();
+    case 1: return arn_sum_kernel<1, U>;
+    case 2: return arn_sum_kernel<2, U>;
+    case 3: return arn_sum_kernel<3, U>;
+    case 4: return arn_sum_kernel<4, U>;
+    case 5: return arn_sum_kernel<5, U>;
+    case 6: return arn_sum_kernel<6, U>;
+    case 7: return arn_sum_kernel<7, U>;
+    default: return arn_sum_kernel<8, U>;
   }
 }
 
@@ -247,12 +243,19 @@ extern "C" int arn_sum_bf16(const void *const *inputs, void *out, int64_t rows, 
   Slabs s;
   for (int p = 0; p < ARNFP8_MAX_P; ++p) s.p[p] = (const u32x4 *)inputs[p < P ? p : 0];
   const int64_t n16 = rows * cols / 8;
+  // 256 lanes; 4 chunks per lane per iteration once that still gives every CU
+  // four workgroups, else 1 (more workgroups for small tensors).  The grid is
+  // capped at 16 workgroups per CU.  Measured on MI355X: P = 8 over 8192 x 7168
+  // 173 us with 4 chunks vs 185 us with 2; P = 4 over 64 x 4096 1.90 us with 1
+  // vs 1.96 us with 2.
   const int threads = 256;
-  const int U = 2;
+  const int64_t cus = device_cus();
+  const bool wide = (n16 + threads * 4 - 1) / (threads * 4) >= 4 * cus;
+  const int U = wide ? 4 : 1;
   int64_t blocks = (n16 + threads * U - 1) / (threads * U);
-  const int64_t cap = (int64_t)device_cus() * 16;
-  if (blocks > cap) blocks = cap;
-  return launch(sum_table(P), dim3((unsigned)blocks), dim3(threads), stream, s, (u32x4 *)out, n16);
+  if (blocks > 16 * cus) blocks = 16 * cus;
+  return launch(wide ? sum_kernel_p<4>(P) : sum_kernel_p<1>(P), dim3((unsigned)blocks),
+                dim3(threads), stream, s, (u32x4 *)out, n16);
 }
 
 extern "C" int arnfp8_run_fmt(const void *const *inputs, const void *residual_in,

@@ -14,7 +14,8 @@ the timed region.  Prints ONE JSON line:
               matches the current kernel source
   cpu_baseline the CPU oracle on the same bytes (rows of the same workload)
   latency_us_per_call  graph-replayed microseconds per call for the decode
-              shapes (P = 4 [32, 7168], P = 8 [128, 8192], P = 2 [4, 256]), the
+              shapes (P = 4 [32, 7168], P = 8 [128, 8192], P = 2 [4, 256]) and of
+              the sum alone (P = 4 [64, 4096]), the
               same buffers every call (cache-warm); latency_us_per_call_cold
               the same with every call reading its own inputs, > 512 MB in all
 
@@ -41,7 +42,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 DEFAULT_WORKLOAD = "prefill_p8_8192x7168"
-DECODE_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "tiny_p2_4x256"]
+DECODE_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "tiny_p2_4x256",
+                    "sum_p4_64x4096"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
 # The device code and the flags it is built with: the committed HBM-counter
 # summary applies only while these are unchanged.
