@@ -18,7 +18,7 @@ __all__ = [
     "arnfp8_run", "arnfp8_run_ex", "arn_sum_bf16", "arnfp8_status_string", "Launch",
     "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW", "arnfp8_stage_bytes",
     "arnfp8_run_share", "SIMD_WIDTH", "arnfp8_run_fmt", "FMT_E4M3FN", "FMT_E5M2", "FMT_MXFP8",
-    "CVT_BF16", "arnfp8_convert_f32",
+    "CVT_BF16", "arnfp8_convert_f32", "STORES_AUTO", "STORES_NT", "STORES_SC1",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -54,7 +54,12 @@ class Launch(ctypes.Structure):
     """``arnfp8_launch``: launch options; 0 in a field means automatic."""
 
     _fields_ = [("variant", ctypes.c_int), ("threads", ctypes.c_int), ("vpt", ctypes.c_int),
-                ("grid", ctypes.c_int)]
+                ("grid", ctypes.c_int), ("stores", ctypes.c_int)]
+
+
+STORES_AUTO = 0
+STORES_NT = 1
+STORES_SC1 = 2
 
 
 _lib = None

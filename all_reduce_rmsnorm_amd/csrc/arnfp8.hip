@@ -91,11 +91,11 @@ SumKernel sum_kernel_p(int P) {
   }
 }
 
-RowKernel row_table(int fmt, int P, int vpt, bool res_in, bool res_out) {
+RowKernel row_table(int fmt, int P, int vpt, bool res_in, bool res_out, bool sc1) {
   switch (fmt) {
-    case ARNFP8_FMT_E5M2: return row_table_e5m2(P, vpt, res_in, res_out);
-    case ARNFP8_FMT_MXFP8: return row_table_mxfp8(P, vpt, res_in, res_out);
-    default: return row_table_e4m3(P, vpt, res_in, res_out);
+    case ARNFP8_FMT_E5M2: return row_table_e5m2(P, vpt, res_in, res_out, sc1);
+    case ARNFP8_FMT_MXFP8: return row_table_mxfp8(P, vpt, res_in, res_out, sc1);
+    default: return row_table_e4m3(P, vpt, res_in, res_out, sc1);
   }
 }
 
@@ -103,6 +103,7 @@ struct RowConfig {
   int threads;
   int vpt;
   int grid;
+  int sc1_stores;
 };
 
 // Smallest chunks-per-lane (1, 2, 4, 8, 16) that fits the row in at most 512
@@ -110,11 +111,12 @@ struct RowConfig {
 // than four rows per CU use all 512 lanes when a lane holds two or more
 // chunks.  Measured on MI355X for 7168-wide rows: 512 x 2 beats 448 x 2 by
 // ~3 % at 1-128 rows (and 1024 x 1 everywhere); 448 x 2 beats 512 x 2 by
-// ~1 % at 8192 rows.
+// ~1 % at 8192 rows.  Row outputs use sc1 stores for large batches and nt
+// stores for small ones (each measured faster in its regime).
 RowConfig pick_row_config(int64_t rows, int c16) {
   static const int vpts[5] = {1, 2, 4, 8, 16};
   const bool small_batch = rows < 4 * (int64_t)device_cus();
-  RowConfig cfg{512, 16, 1};
+  RowConfig cfg{512, 16, 1, small_batch ? 0 : 1};
   for (int i = 0; i < 5; ++i) {
     const int lanes = (c16 + vpts[i] - 1) / vpts[i];
     if (lanes <= 512) {
@@ -193,6 +195,9 @@ int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfi
   }
   if (opt->variant != ARNFP8_VARIANT_AUTO && opt->variant != ARNFP8_VARIANT_ROW)
     return ARNFP8_BAD_CONFIG;
+  if (opt->stores != ARNFP8_STORES_AUTO && opt->stores != ARNFP8_STORES_NT &&
+      opt->stores != ARNFP8_STORES_SC1)
+    return ARNFP8_BAD_CONFIG;
   if (opt->threads < 0 || opt->vpt < 0 || opt->grid < 0) return ARNFP8_BAD_CONFIG;
   if (opt->threads && (opt->threads % 64 != 0 || opt->threads > 1024)) return ARNFP8_BAD_CONFIG;
   if (opt->vpt && opt->vpt != 1 && opt->vpt != 2 && opt->vpt != 4 && opt->vpt != 8 &&
@@ -219,6 +224,10 @@ int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfi
   cfg->grid = opt->grid ? opt->grid : (int)(rows < 65536 ? rows : 65536);
   // A dispatch counts its work-items in 32 bits.
   if ((int64_t)cfg->grid * cfg->threads > (int64_t)UINT32_MAX) return ARNFP8_BAD_CONFIG;
+  if (opt->stores != ARNFP8_STORES_AUTO)
+    cfg->sc1_stores = opt->stores == ARNFP8_STORES_SC1;
+  else if (opt->threads || opt->vpt)  // lanes or chunks given, policy automatic
+    cfg->sc1_stores = rows >= 4 * (int64_t)device_cus();
   return ARNFP8_OK;
 }
 
@@ -277,7 +286,8 @@ extern "C" int arnfp8_run_fmt(const void *const *inputs, const void *residual_in
   RowConfig cfg;  // after validation: the automatic choice queries the device
   st = resolve_row_config(opt, rows, (int)(cols / 8), &cfg);
   if (st != ARNFP8_OK) return st;
-  return launch(row_table(out_format, P, cfg.vpt, residual_in != nullptr, residual_out != nullptr),
+  return launch(row_table(out_format, P, cfg.vpt, residual_in != nullptr, residual_out != nullptr,
+                          cfg.sc1_stores != 0),
                 dim3(cfg.grid), dim3(cfg.threads), stream, a);
 }
 
@@ -358,7 +368,7 @@ extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_
   st = resolve_row_config(nullptr, count, (int)(cols / 8), &cfg);
   if (st != ARNFP8_OK) return st;
   return launch(row_table(ARNFP8_FMT_E4M3FN, P, cfg.vpt, residual_in != nullptr,
-                          residual_out != nullptr),
+                          residual_out != nullptr, cfg.sc1_stores != 0),
                 dim3(cfg.grid), dim3(cfg.threads), stream, a);
 }
 

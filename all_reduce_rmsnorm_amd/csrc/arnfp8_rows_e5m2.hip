@@ -3,8 +3,8 @@
 
 namespace arnfp8 {
 
-RowKernel row_table_e5m2(int P, int vpt, bool res_in, bool res_out) {
-  return RowTable<kFmtE5m2>::get(P, vpt, res_in, res_out);
+RowKernel row_table_e5m2(int P, int vpt, bool res_in, bool res_out, bool sc1) {
+  return RowTable<kFmtE5m2>::get(P, vpt, res_in, res_out, sc1);
 }
 
 }  // namespace arnfp8

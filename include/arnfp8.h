@@ -102,13 +102,21 @@ int arnfp8_run(const void *const *inputs, const void *residual_in, void *residua
 #define ARNFP8_VARIANT_AUTO 0 /* the library's choice from (rows, cols, P)        */
 #define ARNFP8_VARIANT_ROW 1  /* one workgroup per row, rows walked grid-stride  */
 
-/* Launch options for arnfp8_run_ex.  Zero in any field means "automatic". */
+/* Cache policy of the fused kernel's row outputs (arnfp8_launch.stores). */
+#define ARNFP8_STORES_AUTO 0 /* sc1 for batches of >= 4 rows per CU, else nt */
+#define ARNFP8_STORES_NT 1   /* non-temporal stores                          */
+#define ARNFP8_STORES_SC1 2  /* device-scope coherent (sc1) stores           */
+
+/* Launch options for arnfp8_run_ex / arnfp8_run_fmt.  Zero in any field means
+ * "automatic".  No option changes any result. */
 typedef struct arnfp8_launch {
   int variant; /* ARNFP8_VARIANT_*                                               */
   int threads; /* lanes per workgroup: a multiple of 64 in [64, 512], or up to
                   1024 with one chunk per lane (vpt 1)                          */
   int vpt;     /* 16-byte chunks per lane: 1, 2, 4, 8 or 16                    */
-  int grid;    /* workgroups; rows are walked grid-stride (>= 1)               */
+  int grid;    /* workgroups; rows are walked grid-stride (>= 1); grid * threads
+                  must fit in 32 bits                                           */
+  int stores;  /* ARNFP8_STORES_*                                               */
 } arnfp8_launch;
 
 /*

@@ -207,7 +207,7 @@ def test_bad_launch_options_rejected_without_device(L):
     x0, x1 = BASE, BASE + 10 * MB
     for bad in (arn.Launch(threads=96), arn.Launch(threads=1024, vpt=2), arn.Launch(vpt=3),
                 arn.Launch(threads=64, vpt=1), arn.Launch(grid=-1), arn.Launch(variant=9),
-                arn.Launch(threads=512, vpt=2, grid=2**31 - 1)):
+                arn.Launch(threads=512, vpt=2, grid=2**31 - 1), arn.Launch(stores=3)):
         st = L.arnfp8_run_ex(_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 200 * MB,
                              BASE + 300 * MB, 1e-6, 0.0, 1.0, 4, 1024, 2, None, ctypes.byref(bad))
         assert st == 7, (bad.threads, bad.vpt, bad.grid, bad.variant)

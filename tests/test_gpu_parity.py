@@ -341,6 +341,7 @@ def test_unfused_two_launch_chain_is_bitwise_equal(arn, synth):
 
 
 @pytest.mark.parametrize("launch", [dict(threads=960, vpt=1), dict(threads=1024),
+                                    dict(stores=1), dict(stores=2), dict(threads=512, vpt=2, stores=1),
                                     dict(threads=64, vpt=16), dict(threads=128, vpt=8),
                                     dict(threads=256, vpt=4), dict(threads=512, vpt=2),
                                     dict(threads=448, vpt=4, grid=7), dict(threads=320, vpt=4, grid=1)])
