@@ -181,26 +181,55 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // ---------------------------------------------------------------- kernels --
 
-// Sum only: a flat grid-stride stream over all 16-byte chunks of the tensor.
+// Sum only: a flat grid-stride stream over all 16-byte chunks of the tensor,
+// U chunks per lane per iteration.  With U == 4 (large tensors) the result is
+// stored through a buffer resource over the iteration's window with the sc1
+// policy (the fused kernel's large-batch choice); otherwise with nt stores.
 template <int P, int U>
 __global__ __launch_bounds__(256) void arn_sum_kernel(Slabs in, u32x4 *__restrict__ out,
                                                       int64_t n16) {
   const int64_t T = blockDim.x;
   const int64_t stride = (int64_t)gridDim.x * T * U;
-  for (int64_t base = (int64_t)blockIdx.x * T * U + threadIdx.x; base < n16; base += stride) {
-    u32x4 x[U][P];
+  if constexpr (U == 4) {
+    for (int64_t blk = (int64_t)blockIdx.x * T * U; blk < n16; blk += stride) {
+      const int64_t base = blk + threadIdx.x;
+      u32x4 x[U][P];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = base + u * T;
-      if (c < n16) {
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = base + u * T;
+        if (c < n16) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) x[u][p] = load16(in.p[p] + c);
+          for (int p = 0; p < P; ++p) x[u][p] = load16(in.p[p] + c);
+        }
+      }
+      // The window [blk, blk + T * U) clipped to the tensor; stores past its
+      // end are dropped by the buffer range check as well as by the guard.
+      const int64_t left = n16 - blk;
+      const __amdgpu_buffer_rsrc_t w =
+          row_rsrc(out + blk, (int)((left < T * U ? left : T * U) * 16));
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = base + u * T;
+        if (c < n16)
+          buf_store16<true>(w, (int)((threadIdx.x + u * T) * 16), rank_order_sum<P>(x[u]));
       }
     }
+  } else {
+    for (int64_t base = (int64_t)blockIdx.x * T * U + threadIdx.x; base < n16; base += stride) {
+      u32x4 x[U][P];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = base + u * T;
-      if (c < n16) store16(out + c, rank_order_sum<P>(x[u]));
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = base + u * T;
+        if (c < n16) {
+#pragma unroll
+          for (int p = 0; p < P; ++p) x[u][p] = load16(in.p[p] + c);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = base + u * T;
+        if (c < n16) store16(out + c, rank_order_sum<P>(x[u]));
+      }
     }
   }
 }
