@@ -24,10 +24,10 @@
 //    rounded the same way.
 //  * fl32(h * g) stays in registers between the statistics pass and the
 //    quantisation pass: the only global traffic is the algorithmic one.
-//  * (sum h^2, max |h g|) are reduced across the wave with butterfly lane
-//    exchanges and across waves through LDS with one barrier per row; the LDS
-//    slot alternates with the row parity so consecutive rows need no second
-//    barrier.
+//  * (sum h^2, max |h g|) are reduced across the wave with DPP moves inside
+//    each row of 16 lanes and two lane exchanges across rows, then across
+//    waves through LDS with one barrier per row; the LDS slot alternates with
+//    the row parity so consecutive rows need no second barrier.
 //  * fp8 values come from the packed OCP e4m3fn / e5m2 conversions after an
 //    explicit clamp, so a conversion never overflows.
 //  * Every lane reaches every barrier and every lane exchange; guards only
@@ -133,6 +133,10 @@ template <bool SC1>
 __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int byte_off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, SC1 ? kStoreSc1 : kStoreNt);
 }
+template <bool SC1>
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, int byte_off, uint8_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8(v, r, byte_off, 0, SC1 ? kStoreSc1 : kStoreNt);
+}
 
 // Rank-order sum of one chunk: rank 0's value starts the fp32 accumulator,
 // ranks 1..P-1 are added in order, and the total is rounded once to bf16.
@@ -167,15 +171,41 @@ __device__ __forceinline__ u32x4 add_bf16(u32x4 s, u32x4 r) {
   return h;
 }
 
-// Butterfly reductions across the 64 lanes of a wave; every lane gets the result.
+// DPP lane exchanges inside a row of 16 lanes (VALU moves, no LDS): the
+// partner lane is lane ^ 1 (quad_perm [1,0,3,2]), lane ^ 2 (quad_perm
+// [2,3,0,1]), the mirror within 8 lanes, or the mirror within 16 lanes.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false));
+}
+
+// Reductions across the 64 lanes of a wave; every lane gets the result.
+// Within a row of 16 lanes: xor 1, xor 2 (the quad), then the 8-lane and
+// 16-lane mirrors, which pair each lane with one in the other half; across
+// rows: lane exchanges at distance 16 and 32.  The order of the additions
+// is fixed, so the sum is deterministic.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  v += dpp<kDppQuadXor1>(v);
+  v += dpp<kDppQuadXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
   return v;
 }
 
@@ -328,6 +358,8 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
         row_rsrc(RES_OUT ? (const void *)(a.res_out + base) : (const void *)a.gamma,
                  RES_OUT ? a.c16 * 16 : 0);
     const __amdgpu_buffer_rsrc_t qout = row_rsrc(a.out + base, a.c16 * 8);
+    const __amdgpu_buffer_rsrc_t mxout =
+        FMT == kFmtMx ? row_rsrc(a.mx_scales + row * (int64_t)(a.c16 >> 2), a.c16 >> 2) : qout;
     float hg[KEEP_HG ? VPT : 1][8];
     u32x4 hk[KEEP_HG ? 1 : VPT];
     float ss = 0.0f, mx = 0.0f;
@@ -427,13 +459,13 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
             y[e] = y[e] * r;
             bmax = fmaxf(bmax, fabsf(y[e]));
           }
-          bmax = fmaxf(bmax, __shfl_xor(bmax, 1, 64));
-          bmax = fmaxf(bmax, __shfl_xor(bmax, 2, 64));
+          bmax = fmaxf(bmax, dpp<kDppQuadXor1>(bmax));
+          bmax = fmaxf(bmax, dpp<kDppQuadXor2>(bmax));
           const int ex = mx_shared_exp(bmax);
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             q[e] = fminf(fmaxf(__builtin_amdgcn_ldexpf(y[e], -ex), -448.0f), 448.0f);
-          if (c <= last && (t & 3) == 0) a.mx_scales[row * (int64_t)(a.c16 >> 2) + (c >> 2)] = (uint8_t)(ex + 127);
+          if (c <= last && (t & 3) == 0) buf_store1<SC1>(mxout, c >> 2, (uint8_t)(ex + 127));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
