@@ -470,6 +470,10 @@ def main():
             "copy_1GiB_gbs": round(2 * (1 << 30) / (cp_k * 1e-3) / 1e9, 1),
             "sum_only_same_slabs_gbs": round((2 * w.P + 2) * w.numel / (sm_k * 1e-3) / 1e9, 1),
         }
+    props = torch.cuda.get_device_properties(dev)
+    result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                        "compute_units": props.multi_processor_count,
+                        "hbm_gib": round(props.total_memory / 2**30, 1)}
     if not args.no_latency:
         lat = {}
         for name in DECODE_WORKLOADS:
