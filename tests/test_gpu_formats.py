@@ -152,3 +152,33 @@ def test_format_errors(arn):
     with pytest.raises(arn.ArnFp8Error) as e:
         arn.arnfp8_run_fmt([x], None, None, out, s, g, 1e-6, 0.0, 1.0, out_format=7)
     assert e.value.status == 9
+
+
+@pytest.mark.parametrize("stores", [1, 2])
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e5m2", "mxfp8"])
+def test_every_format_under_both_store_policies(arn, orc, fmt, stores):
+    """Each output format with nt (1) and sc1 (2) row stores on a ragged shape."""
+    rows, cols, P = 21, 7168 + 64 * 3, 4
+    print(f"[{fmt}] stores={stores}", flush=True)
+    xs, res, gamma = _case(11 * stores + len(fmt), rows, cols, P)
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    res_out = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    code = {"e4m3fn": arn.FMT_E4M3FN, "e5m2": arn.FMT_E5M2, "mxfp8": arn.FMT_MXFP8}[fmt]
+    if fmt == "mxfp8":
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=DEV)
+    else:
+        scales = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    arn.arnfp8_run_fmt([x.to(DEV) for x in xs], res.to(DEV), res_out, out, scales, gamma.to(DEV),
+                       1e-6, 0.0, 1200.0, out_format=code, launch=dict(stores=stores))
+    torch.cuda.synchronize()
+    if fmt == "mxfp8":
+        check_mx(orc, xs, res, gamma, out, scales, res_out)
+        return
+    fn = orc.arnfp8 if fmt == "e4m3fn" else orc.arnfp8_e5m2
+    q, s, h = fn([_bits(x) for x in xs], _bits(gamma), 1e-6, 0.0, 1200.0, residual_in=_bits(res))
+    assert_bits_equal(_bits(res_out), h, "residual_out")
+    assert_scales_close(scales.cpu().numpy(), s)
+    if fmt == "e4m3fn":
+        assert_fp8_close(out.cpu().numpy(), q)
+    else:
+        assert_e5m2_close(out.cpu().numpy(), q)
