@@ -255,11 +255,11 @@ def summarize_pmc(directory: str, out_path: str, workload: str):
         f"{calib_bytes} bytes (read {calib_bytes} B, write {calib_bytes} B).",
         "Commands (from the repository root, on one MI355X):",
         "",
-        "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o fetch -- "
+        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/pmc_fetch -o fetch -- "
         "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-latency --pmc-calib",
-        "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o write -- "
+        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {directory}/pmc_write -o write -- "
         "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-latency --pmc-calib",
-        "    python bench.py --summarize-pmc gpurun_out",
+        f"    python bench.py --summarize-pmc {directory}",
         "",
         "| counter | fused kernel (mean per dispatch) | copy kernel | scale factor | scaled bytes |",
         "|---|---|---|---|---|",
