@@ -106,17 +106,34 @@ def library() -> ctypes.CDLL:
     return _lib
 
 
-def _ptr(t):
-    """Device pointer of a tensor (or a raw integer address, or None)."""
+_BF16 = ("bfloat16",)
+_FP8 = ("float8_e4m3fn", "float8_e5m2", "uint8", "int8")
+_F32 = ("float32",)
+_U8 = ("uint8", "int8")
+
+
+def _ptr(t, kinds=None, what="tensor"):
+    """Device pointer of a tensor (or a raw integer address, or None).
+
+    Tensors must be dense (contiguous) and, when ``kinds`` is given, of one of
+    those dtypes, and on the device: the library reads plain row-major device
+    memory.
+    """
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous (the library reads dense row-major memory)")
+    if kinds is not None and str(t.dtype).replace("torch.", "") not in kinds:
+        raise TypeError(f"{what} has dtype {t.dtype}; expected one of {', '.join(kinds)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device (cuda) tensor, got {t.device}")
     return t.data_ptr()
 
 
 def _ptr_array(inputs):
-    ptrs = [_ptr(x) for x in inputs]
+    ptrs = [_ptr(x, _BF16, f"inputs[{i}]") for i, x in enumerate(inputs)]
     return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
 
 
@@ -157,8 +174,10 @@ def arnfp8_run(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps, w
     Runs on ``stream`` (default: PyTorch's current stream).
     """
     rows, cols, P = _shape(inputs, rows, cols, P)
-    st = library().arnfp8_run(_ptr_array(inputs), _ptr(residual_in), _ptr(residual_out),
-                              _ptr(out_fp8), _ptr(scales), _ptr(gamma), float(eps),
+    st = library().arnfp8_run(_ptr_array(inputs), _ptr(residual_in, _BF16, "residual_in"),
+                              _ptr(residual_out, _BF16, "residual_out"),
+                              _ptr(out_fp8, _FP8, "out_fp8"), _ptr(scales, _F32, "scales"),
+                              _ptr(gamma, _BF16, "gamma"), float(eps),
                               float(weight_offset), float(scale_ub), rows, cols, P,
                               _stream(stream))
     if st != 0:
@@ -173,8 +192,10 @@ def arnfp8_run_ex(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps
     if isinstance(launch, dict):
         launch = Launch(**launch)
     opt = ctypes.byref(launch) if launch is not None else None
-    st = library().arnfp8_run_ex(_ptr_array(inputs), _ptr(residual_in), _ptr(residual_out),
-                                 _ptr(out_fp8), _ptr(scales), _ptr(gamma), float(eps),
+    st = library().arnfp8_run_ex(_ptr_array(inputs), _ptr(residual_in, _BF16, "residual_in"),
+                                 _ptr(residual_out, _BF16, "residual_out"),
+                                 _ptr(out_fp8, _FP8, "out_fp8"), _ptr(scales, _F32, "scales"),
+                                 _ptr(gamma, _BF16, "gamma"), float(eps),
                                  float(weight_offset), float(scale_ub), rows, cols, P,
                                  _stream(stream), opt)
     if st != 0:
@@ -184,7 +205,8 @@ def arnfp8_run_ex(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps
 def arn_sum_bf16(inputs, out, rows=None, cols=None, P=None, stream=None) -> None:
     """Rank-order fp32 sum of P bf16 slabs, rounded once to bf16, into ``out``."""
     rows, cols, P = _shape(inputs, rows, cols, P)
-    st = library().arn_sum_bf16(_ptr_array(inputs), _ptr(out), rows, cols, P, _stream(stream))
+    st = library().arn_sum_bf16(_ptr_array(inputs), _ptr(out, _BF16, "out"), rows, cols, P,
+                                _stream(stream))
     if st != 0:
         raise ArnFp8Error("arn_sum_bf16", st)
 
@@ -198,8 +220,10 @@ def arnfp8_run_share(inputs, residual_in, residual_out, staging, gamma, eps, wei
                      scale_ub, rows=None, cols=None, P=None, ngpus=1, rank=0, stream=None) -> None:
     """The fused epilogue on rank ``rank``'s row share, fp8 rows + scales into ``staging``."""
     rows, cols, P = _shape(inputs, rows, cols, P)
-    st = library().arnfp8_run_share(_ptr_array(inputs), _ptr(residual_in), _ptr(residual_out),
-                                    _ptr(staging), _ptr(gamma), float(eps), float(weight_offset),
+    st = library().arnfp8_run_share(_ptr_array(inputs), _ptr(residual_in, _BF16, "residual_in"),
+                                    _ptr(residual_out, _BF16, "residual_out"),
+                                    _ptr(staging, _U8, "staging"), _ptr(gamma, _BF16, "gamma"),
+                                    float(eps), float(weight_offset),
                                     float(scale_ub), rows, cols, P, int(ngpus), int(rank),
                                     _stream(stream))
     if st != 0:
@@ -216,8 +240,13 @@ def arnfp8_run_fmt(inputs, residual_in, residual_out, out_fp8, scales, gamma, ep
     if isinstance(launch, dict):
         launch = Launch(**launch)
     opt = ctypes.byref(launch) if launch is not None else None
-    st = library().arnfp8_run_fmt(_ptr_array(inputs), _ptr(residual_in), _ptr(residual_out),
-                                  _ptr(out_fp8), _ptr(scales), _ptr(gamma), float(eps),
+    # an unknown format is left to the library, which reports it as BAD_FORMAT
+    scale_kinds = {FMT_MXFP8: _U8, FMT_E4M3FN: _F32, FMT_E5M2: _F32}.get(int(out_format))
+    st = library().arnfp8_run_fmt(_ptr_array(inputs), _ptr(residual_in, _BF16, "residual_in"),
+                                  _ptr(residual_out, _BF16, "residual_out"),
+                                  _ptr(out_fp8, _FP8, "out_fp8"),
+                                  _ptr(scales, scale_kinds, "scales"), _ptr(gamma, _BF16, "gamma"),
+                                  float(eps),
                                   float(weight_offset), float(scale_ub), rows, cols, P,
                                   int(out_format), _stream(stream), opt)
     if st != 0:
@@ -228,6 +257,8 @@ def arnfp8_convert_f32(inp, out, fmt, n=None, stream=None) -> None:
     """The kernels' conversion step alone: fp32 ``inp`` -> ``out`` in format
     ``fmt`` (FMT_E4M3FN, FMT_E5M2: clamped; CVT_BF16), round to nearest even."""
     n = int(inp.numel()) if n is None else int(n)
-    st = library().arnfp8_convert_f32(_ptr(inp), _ptr(out), n, int(fmt), _stream(stream))
+    out_kinds = ("bfloat16", "int16", "uint16") if int(fmt) == CVT_BF16 else _FP8
+    st = library().arnfp8_convert_f32(_ptr(inp, _F32, "inp"), _ptr(out, out_kinds, "out"), n,
+                                      int(fmt), _stream(stream))
     if st != 0:
         raise ArnFp8Error("arnfp8_convert_f32", st)

@@ -217,3 +217,22 @@ def test_bad_launch_options_rejected_without_device(L):
     st = L.arnfp8_run_fmt(_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 200 * MB,
                           BASE + 300 * MB, 1e-6, 0.0, 1.0, 4, 1000, 2, 2, None, None)
     assert st == BAD_SHAPE  # MXFP8 needs cols % 32 == 0
+
+
+def test_binding_refuses_what_the_library_cannot_read():
+    import torch
+
+    import all_reduce_rmsnorm_amd as arn
+
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    out = torch.zeros((4, 64), dtype=torch.uint8)
+    s = torch.zeros((4,), dtype=torch.float32)
+    g = torch.zeros((64,), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="contiguous"):
+        arn.arnfp8_run([x[:, 8:]], None, None, out, s, g, 1e-6, 0.0, 1.0, rows=4, cols=56)
+    with pytest.raises(TypeError, match="dtype"):
+        arn.arnfp8_run([x.float()], None, None, out, s, g, 1e-6, 0.0, 1.0)
+    with pytest.raises(TypeError, match="dtype"):
+        arn._ptr(s.double(), arn._F32, "scales")
+    with pytest.raises(ValueError, match="device"):
+        arn.arnfp8_run([x], None, None, out, s, g, 1e-6, 0.0, 1.0)

@@ -319,9 +319,13 @@ def test_errors_raise_before_launch(arn):
     with pytest.raises(arn.ArnFp8Error) as e:
         arn.arnfp8_run([x, x], None, x, out, s, g, 1e-6, 0.0, 1.0)  # residual_out aliases inputs
     assert e.value.status == 5
+    flat = torch.zeros((4 * 64 + 4,), dtype=torch.bfloat16, device=DEV)
+    shifted = flat[4:].view(4, 64)  # contiguous, but 8 bytes past a 16-byte boundary
     with pytest.raises(arn.ArnFp8Error) as e:
-        arn.arnfp8_run([x[:, 4:]], None, None, out, s, g, 1e-6, 0.0, 1.0, rows=4, cols=56)
+        arn.arnfp8_run([shifted], None, None, out, s, g, 1e-6, 0.0, 1.0)
     assert e.value.status == 2
+    with pytest.raises(ValueError):  # a strided view is refused by the binding
+        arn.arnfp8_run([x[:, 8:]], None, None, out, s, g, 1e-6, 0.0, 1.0, rows=4, cols=56)
     torch.cuda.synchronize()
 
 
