@@ -193,6 +193,59 @@ def cpu_baseline(w, d, torch, min_seconds=10.0, max_passes=3):
     }
 
 
+def host_cpu():
+    """Model name and the CPUs this process may run on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "usable_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_oracle_threaded(w, d, torch, passes=3, max_threads=16):
+    """The same oracle, unchanged, with the workload's rows split into blocks
+    that a thread pool hands to it (the C calls run without the interpreter
+    lock).  A second CPU figure beside the single-threaded baseline."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from all_reduce_rmsnorm_amd import synth
+
+    threads = max(1, min(max_threads, len(os.sched_getaffinity(0))))
+    block = max(1, -(-w.rows // (4 * threads)))
+    gamma = synth.bf16_bits(d["gamma"])
+    blocks = []
+    for r0 in range(0, w.rows, block):
+        r1 = min(w.rows, r0 + block)
+        xs = [synth.bf16_bits(x[r0:r1]) for x in d["inputs"]]
+        res = None if d["residual"] is None else synth.bf16_bits(d["residual"][r0:r1])
+        blocks.append((xs, res))
+
+    def one(b):
+        xs, res = b
+        if w.sum_only:
+            oracle.sum_bf16(xs)
+        else:
+            oracle.arnfp8(xs, gamma, w.eps, w.weight_offset, w.scale_ub, residual_in=res)
+
+    times = []
+    with ThreadPoolExecutor(threads) as pool:
+        for _ in range(passes):
+            t = time.perf_counter()
+            list(pool.map(one, blocks))
+            times.append(time.perf_counter() - t)
+    per_pass = sorted(times)[len(times) // 2]
+    return {"value": round(w.algorithmic_bytes() / per_pass / 1e9, 4), "unit": "GB/s",
+            "threads": threads, "ms_per_step": round(per_pass * 1e3, 3),
+            "sample": f"every row of {w.name} in {len(blocks)} blocks, median of {passes} passes",
+            "host_cpu": host_cpu()}
+
+
 # ------------------------------------------------------- HBM counters ------
 
 def read_traffic(kernel_hash: str):
@@ -493,6 +546,8 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, d, torch)
         log(f"bench: cpu baseline {result['cpu_baseline']}")
+        result["cpu_oracle_threaded"] = cpu_oracle_threaded(w, d, torch)
+        log(f"bench: oracle on a thread pool {result['cpu_oracle_threaded']}")
     print(json.dumps(result), flush=True)
     return 0
 

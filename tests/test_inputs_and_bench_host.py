@@ -102,3 +102,23 @@ def test_summarize_pmc_scales_by_the_copy(tmp_path):
     # FETCH scaled x2 (copy read 1 GiB, counter 512 MiB), WRITE x1
     want = int(round(500000 * 1024 * 2.0 + 100000 * 1024 * 1.0))
     assert f"traffic_bytes_per_launch: {want}" in text
+
+
+def test_cpu_figures_cover_every_row_and_agree_in_units():
+    """Both CPU figures time the oracle over the whole workload and report the
+    same algorithmic bytes per pass."""
+    import torch
+
+    import bench
+    from all_reduce_rmsnorm_amd import synth
+
+    w = synth.WORKLOADS["decode_p4_32x7168"]
+    d = synth.make_inputs(w)
+    one = bench.cpu_baseline(w, d, torch, min_seconds=0.0, max_passes=1)
+    many = bench.cpu_oracle_threaded(w, d, torch, passes=1)
+    assert one["cores"] == 1 and one["kind"] == "oracle" and one["unit"] == many["unit"] == "GB/s"
+    for r in (one, many):
+        gbs = w.algorithmic_bytes() / (r["ms_per_step"] * 1e-3) / 1e9
+        assert abs(gbs - r["value"]) <= 1e-3 * gbs + 1e-4
+    assert 1 <= many["threads"] <= 16
+    assert "32 rows" in one["sample"] or "(32 rows)" in one["sample"]
