@@ -111,12 +111,12 @@ struct RowConfig {
 // than four rows per CU use all 512 lanes when a lane holds two or more
 // chunks.  Measured on MI355X for 7168-wide rows: 512 x 2 beats 448 x 2 by
 // ~3 % at 1-128 rows (and 1024 x 1 everywhere); 448 x 2 beats 512 x 2 by
-// ~1 % at 8192 rows.  Row outputs use sc1 stores for large batches and nt
-// stores for small ones (each measured faster in its regime).
+// ~1 % at 8192 rows.  Row outputs use nt stores (the fastest policy when
+// the output buffers are not cache-resident, at every batch size measured).
 RowConfig pick_row_config(int64_t rows, int c16) {
   static const int vpts[5] = {1, 2, 4, 8, 16};
   const bool small_batch = rows < 4 * (int64_t)device_cus();
-  RowConfig cfg{512, 16, 1, small_batch ? 0 : 1};
+  RowConfig cfg{512, 16, 1, 0};
   for (int i = 0; i < 5; ++i) {
     const int lanes = (c16 + vpts[i] - 1) / vpts[i];
     if (lanes <= 512) {
@@ -224,10 +224,7 @@ int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfi
   cfg->grid = opt->grid ? opt->grid : (int)(rows < 65536 ? rows : 65536);
   // A dispatch counts its work-items in 32 bits.
   if ((int64_t)cfg->grid * cfg->threads > (int64_t)UINT32_MAX) return ARNFP8_BAD_CONFIG;
-  if (opt->stores != ARNFP8_STORES_AUTO)
-    cfg->sc1_stores = opt->stores == ARNFP8_STORES_SC1;
-  else if (opt->threads || opt->vpt)  // lanes or chunks given, policy automatic
-    cfg->sc1_stores = rows >= 4 * (int64_t)device_cus();
+  cfg->sc1_stores = opt->stores == ARNFP8_STORES_SC1;
   return ARNFP8_OK;
 }
 

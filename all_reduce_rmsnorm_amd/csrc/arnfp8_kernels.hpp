@@ -107,12 +107,15 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
 __device__ __forceinline__ u32x4 load16(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store16(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
-// The fused kernel's row outputs go through buffer stores so that the cache
-// policy can be chosen per launch: non-temporal (nt), or sc1 (device-scope
-// coherence).  Measured on MI355X: sc1 stores cut the 8192 x 7168, P = 8
-// launch from ~204.5 to ~198 us; for decode batches nt stores are faster,
-// above all when the inputs are not in cache (P = 4 [32, 7168]: 4.9 us nt,
-// 5.2 us with the default policy).
+// Row outputs go through buffer stores so that the cache policy can be chosen
+// per launch: non-temporal (nt, the default) or sc1 (device-scope coherence).
+// Measured on MI355X with a fresh set of output buffers on every call (the
+// usual case: the outputs do not stay in the 256 MB Infinity Cache between
+// calls), nt stores are the fastest policy: 8192 x 7168, P = 8 takes ~205 us
+// with nt, ~211 us with sc1 and ~212 us with the default policy.  sc1 wins
+// (~197 us) only when the same output buffers are rewritten while they are
+// still cache-resident.  For decode batches nt is also the fastest (P = 4
+// [32, 7168], inputs not in cache: 4.9 us nt, 5.2 us default policy).
 constexpr int kStoreNt = 2;    // cache-policy operand bit of nt
 constexpr int kStoreSc1 = 16;  // cache-policy operand bit of sc1
 // Word 3 of a raw (untyped, unswizzled, stride-0) buffer resource on
@@ -213,8 +216,8 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Sum only: a flat grid-stride stream over all 16-byte chunks of the tensor,
 // U chunks per lane per iteration.  With U == 4 (large tensors) the result is
-// stored through a buffer resource over the iteration's window with the sc1
-// policy (the fused kernel's large-batch choice); otherwise with nt stores.
+// stored with nt buffer stores through a resource over the iteration's
+// window; otherwise with plain nt stores.
 template <int P, int U>
 __global__ __launch_bounds__(256) void arn_sum_kernel(Slabs in, u32x4 *__restrict__ out,
                                                       int64_t n16) {
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(256) void arn_sum_kernel(Slabs in, u32x4 *__restric
       for (int u = 0; u < U; ++u) {
         const int64_t c = base + u * T;
         if (c < n16)
-          buf_store16<true>(w, (int)((threadIdx.x + u * T) * 16), rank_order_sum<P>(x[u]));
+          buf_store16<false>(w, (int)((threadIdx.x + u * T) * 16), rank_order_sum<P>(x[u]));
       }
     }
   } else {

@@ -4,7 +4,9 @@
 A step is one ``arnfp8_run`` call over the prefill workload (P = 8 bf16 slabs
 [8192, 7168] ~ N(0, 0.5) with 0.1 % outliers x100, bf16 residual ~ N(0, 1),
 gamma ~ U(0.8, 1.2), eps 1e-6, scale_ub 64), all inputs resident in HBM before
-the timed region.  Prints ONE JSON line:
+the timed region.  Each call writes the next of several output buffer sets,
+together larger than twice the 256 MB Infinity Cache, so no call finds its
+outputs in cache.  Prints ONE JSON line:
 
   value       algorithmic HBM bytes per step / wall time per step   (GB/s)
   roofline    the kernel's algorithmic bytes / its average duration from HIP
@@ -30,6 +32,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import itertools
 import json
 import os
 import re
@@ -45,10 +48,12 @@ DEFAULT_WORKLOAD = "prefill_p8_8192x7168"
 DECODE_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "tiny_p2_4x256",
                     "sum_p4_64x4096"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
-# The device code and the flags it is built with: the committed HBM-counter
-# summary applies only while these are unchanged.
+# The device code, the host code that picks its launch shape and cache
+# policy, and the build flags: the committed HBM-counter summary applies only
+# while these are unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_kernels.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_tables.hpp"),
+                  os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8.hip"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
 
 
@@ -66,24 +71,54 @@ def log(msg):
 
 # --------------------------------------------------------------- GPU side --
 
-def alloc_workload(w, torch, dev):
+# Outputs rotate over enough buffer sets that together they exceed twice the
+# 256 MB Infinity Cache: every call then writes buffers that are not cache-
+# resident, as in a model, where other work runs between two calls.
+CACHE_FLUSH_BYTES = 512 << 20
+MAX_OUT_SETS = 8
+
+
+def out_sets_for(w) -> int:
+    per = w.numel * (2 if w.sum_only else 1 + (2 if w.residual_std is not None else 0))
+    return max(1, min(MAX_OUT_SETS, -(-CACHE_FLUSH_BYTES // max(1, per))))
+
+
+def alloc_workload(w, torch, dev, out_sets: int = 1):
+    """Inputs of workload `w` on `dev`, and `out_sets` sets of output buffers
+    (d["outs"]; d["out"], d["scales"], d["res_out"], d["sum_out"] are set 0)."""
     from all_reduce_rmsnorm_amd import synth
 
     d = synth.make_inputs(w, device=dev)
     rows, cols = w.rows, w.cols
-    d["out"] = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=dev)
-    d["scales"] = torch.empty((rows,), dtype=torch.float32, device=dev)
-    d["res_out"] = (torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-                    if d["residual"] is not None else None)
-    d["sum_out"] = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    d["outs"] = []
+    for _ in range(out_sets):
+        o = {"out": None, "scales": None, "res_out": None, "sum_out": None}
+        if w.sum_only:
+            o["sum_out"] = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+        else:
+            o["out"] = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=dev)
+            o["scales"] = torch.empty((rows,), dtype=torch.float32, device=dev)
+            if d["residual"] is not None:
+                o["res_out"] = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+        d["outs"].append(o)
+    d.update(d["outs"][0])
     return d
 
 
+def rotating(fns):
+    """One callable that calls fns[0], fns[1], ... in turn."""
+    it = itertools.cycle(fns)
+    return lambda: next(it)()
+
+
 def step_fn(w, d, arn):
-    if w.sum_only:
-        return lambda: arn.arn_sum_bf16(d["inputs"], d["sum_out"])
-    return lambda: arn.arnfp8_run(d["inputs"], d["residual"], d["res_out"], d["out"], d["scales"],
-                                  d["gamma"], w.eps, w.weight_offset, w.scale_ub)
+    """One step of workload `w`, each call writing the next output set."""
+    def one(o):
+        if w.sum_only:
+            return lambda: arn.arn_sum_bf16(d["inputs"], o["sum_out"])
+        return lambda: arn.arnfp8_run(d["inputs"], d["residual"], o["res_out"], o["out"],
+                                      o["scales"], d["gamma"], w.eps, w.weight_offset, w.scale_ub)
+    return rotating([one(o) for o in d["outs"]])
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -119,9 +154,11 @@ def graph_us_per_call_cold(torch, w, arn, dev, min_bytes=600 << 20, max_sets=400
     for k in range(nsets):
         dk = dict(base)
         dk["inputs"] = [x.clone() for x in base["inputs"]]
+        o = {key: (None if t is None else torch.empty_like(t)) for key, t in base["outs"][0].items()}
         if base["residual"] is not None:
             dk["residual"] = base["residual"].clone()
-            dk["res_out"] = dk["residual"]  # in place, as the decode workloads update it
+            o["res_out"] = dk["residual"]  # in place, as the decode workloads update it
+        dk["outs"] = [o]
         sets.append(step_fn(w, dk, arn))
     us = graph_us_per_call(torch, lambda: [f() for f in sets], calls=1, reps=5) / nsets
     del sets, base
@@ -434,7 +471,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     log(f"bench: workload {w.name}, steps {args.steps}, warmup {args.warmup}")
-    d = alloc_workload(w, torch, dev)
+    n_out = out_sets_for(w)
+    d = alloc_workload(w, torch, dev, out_sets=n_out)
     torch.cuda.synchronize()
     fn = step_fn(w, d, arn)
     ms_per_step, kern_ms = time_steps(torch, fn, args.steps, args.warmup)
@@ -461,6 +499,7 @@ def main():
         "dtype": "f32",
         "io_dtypes": "bf16 in, bf16 residual out, e4m3fn + f32 scales out" if not w.sum_only else "bf16 in, bf16 out",
         "data": "synthetic (seeded; inputs resident in HBM)",
+        "output_sets": n_out,
         "config": {"workload": w.name, "P": w.P, "rows": w.rows, "cols": w.cols,
                    "residual": w.residual_std is not None, "eps": w.eps,
                    "weight_offset": w.weight_offset, "scale_ub": w.scale_ub,
@@ -473,11 +512,15 @@ def main():
     if not w.sum_only and not args.no_latency:
         # The unfused chain the fusion removes: the sum is written to HBM as
         # bf16 and read back by a second launch (the fused kernel with P = 1).
-        s_buf = d["sum_out"]
-        unfused = lambda: (arn.arn_sum_bf16(d["inputs"], s_buf),
-                           arn.arnfp8_run([s_buf], d["residual"], d["res_out"], d["out"],
-                                          d["scales"], d["gamma"], w.eps, w.weight_offset,
-                                          w.scale_ub))
+        s_bufs = [torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=dev)
+                  for _ in d["outs"]]
+
+        def unfused_one(o, s_buf):
+            return lambda: (arn.arn_sum_bf16(d["inputs"], s_buf),
+                            arn.arnfp8_run([s_buf], d["residual"], o["res_out"], o["out"],
+                                           o["scales"], d["gamma"], w.eps, w.weight_offset,
+                                           w.scale_ub))
+        unfused = rotating([unfused_one(o, sb) for o, sb in zip(d["outs"], s_bufs)])
         un_ms, _ = time_steps(torch, unfused, max(5, args.steps // 2), 3)
         result["unfused_two_launch"] = {
             "us_per_call": round(un_ms * 1e3, 2),
@@ -488,11 +531,17 @@ def main():
         # The other output formats on the same workload and bytes (the MX
         # block scales replace the per-row scales: rows * cols / 32 bytes).
         fmt_out = {}
-        mx_scales = torch.empty((w.rows, w.cols // 32), dtype=torch.uint8, device=dev)
-        for name, fmt, sc in (("e5m2", arn.FMT_E5M2, d["scales"]), ("mxfp8", arn.FMT_MXFP8, mx_scales)):
-            _, f_k = time_steps(torch, lambda: arn.arnfp8_run_fmt(
-                d["inputs"], d["residual"], d["res_out"], d["out"], sc, d["gamma"], w.eps,
-                w.weight_offset, w.scale_ub, out_format=fmt), max(10, args.steps // 2), 3)
+        mx_scales = [torch.empty((w.rows, w.cols // 32), dtype=torch.uint8, device=dev)
+                     for _ in d["outs"]]
+
+        def fmt_one(o, sc, fmt):
+            return lambda: arn.arnfp8_run_fmt(d["inputs"], d["residual"], o["res_out"], o["out"],
+                                              sc, d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                                              out_format=fmt)
+        for name, fmt in (("e5m2", arn.FMT_E5M2), ("mxfp8", arn.FMT_MXFP8)):
+            scs = mx_scales if fmt == arn.FMT_MXFP8 else [o["scales"] for o in d["outs"]]
+            f = rotating([fmt_one(o, sc, fmt) for o, sc in zip(d["outs"], scs)])
+            _, f_k = time_steps(torch, f, max(10, args.steps // 2), 3)
             fmt_out[f"{name}_us_per_call"] = round(f_k * 1e3, 2)
         result["formats"] = fmt_out
         del mx_scales
@@ -502,12 +551,18 @@ def main():
         stg = torch.empty((arn.arnfp8_stage_bytes(w.rows, w.cols, ngpus),), dtype=torch.uint8,
                           device=dev)
         share_rows = -(-w.rows // ngpus)
-        sh_ms, sh_k = time_steps(torch, lambda: arn.arnfp8_run_share(
-            d["inputs"], d["residual"], d["res_out"], stg, d["gamma"], w.eps, w.weight_offset,
-            w.scale_ub, ngpus=ngpus, rank=3), max(10, args.steps), 3)
+
+        # The ranks' shares in turn: each call reads other rows and writes
+        # another staging slot, so no call finds its inputs in cache.
+        def share_one(rank):
+            return lambda: arn.arnfp8_run_share(
+                d["inputs"], d["residual"], d["res_out"], stg, d["gamma"], w.eps,
+                w.weight_offset, w.scale_ub, ngpus=ngpus, rank=rank)
+        sh_ms, sh_k = time_steps(torch, rotating([share_one(r) for r in range(ngpus)]),
+                                 max(16, args.steps), 3)
         share_bytes = (2 * w.P + 4 + 1) * share_rows * w.cols + 4 * share_rows + 2 * w.cols
         result["two_stage_share"] = {
-            "ngpus": ngpus, "rank": 3, "rows": share_rows,
+            "ngpus": ngpus, "rank": "0-7 in turn", "rows": share_rows,
             "us_per_call": round(sh_k * 1e3, 2),
             "gbs": round(share_bytes / (sh_k * 1e-3) / 1e9, 1),
         }
@@ -518,7 +573,9 @@ def main():
         dst = torch.empty_like(src)
         cp_ms, cp_k = time_steps(torch, lambda: arn.arn_sum_bf16([src], dst), 10, 3)
         del src, dst
-        sm_ms, sm_k = time_steps(torch, lambda: arn.arn_sum_bf16(d["inputs"], s_buf), 10, 3)
+        sm_ms, sm_k = time_steps(torch, rotating([(lambda sb=sb: arn.arn_sum_bf16(d["inputs"], sb))
+                                                  for sb in s_bufs]), 10, 3)
+        del s_bufs
         result["reference_kernels"] = {
             "copy_1GiB_gbs": round(2 * (1 << 30) / (cp_k * 1e-3) / 1e9, 1),
             "sum_only_same_slabs_gbs": round((2 * w.P + 2) * w.numel / (sm_k * 1e-3) / 1e9, 1),

@@ -102,8 +102,11 @@ int arnfp8_run(const void *const *inputs, const void *residual_in, void *residua
 #define ARNFP8_VARIANT_AUTO 0 /* the library's choice from (rows, cols, P)        */
 #define ARNFP8_VARIANT_ROW 1  /* one workgroup per row, rows walked grid-stride  */
 
-/* Cache policy of the fused kernel's row outputs (arnfp8_launch.stores). */
-#define ARNFP8_STORES_AUTO 0 /* sc1 for batches of >= 4 rows per CU, else nt */
+/* Cache policy of the fused kernel's row outputs (arnfp8_launch.stores).  nt
+ * is the fastest when the output buffers are not cache-resident between calls;
+ * sc1 is faster only when the same buffers are rewritten while still cached.
+ * The policy never changes a result. */
+#define ARNFP8_STORES_AUTO 0 /* the library's choice: currently nt            */
 #define ARNFP8_STORES_NT 1   /* non-temporal stores                          */
 #define ARNFP8_STORES_SC1 2  /* device-scope coherent (sc1) stores           */
 
