@@ -105,6 +105,19 @@ def alloc_workload(w, torch, dev, out_sets: int = 1):
     return d
 
 
+def input_sha256(d, torch) -> str:
+    """SHA-256 over the bytes of every input tensor (slabs in rank order, the
+    residual if any, gamma), so a run records exactly what it measured."""
+    h = hashlib.sha256()
+    ts = list(d["inputs"]) + ([d["residual"]] if d["residual"] is not None else []) + [d["gamma"]]
+    for t in ts:
+        flat = t.reshape(-1).view(torch.uint8)
+        step = 64 << 20
+        for i in range(0, flat.numel(), step):
+            h.update(flat[i:i + step].cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
 def rotating(fns):
     """One callable that calls fns[0], fns[1], ... in turn."""
     it = itertools.cycle(fns)
@@ -503,7 +516,7 @@ def main():
         "config": {"workload": w.name, "P": w.P, "rows": w.rows, "cols": w.cols,
                    "residual": w.residual_std is not None, "eps": w.eps,
                    "weight_offset": w.weight_offset, "scale_ub": w.scale_ub,
-                   "algorithmic_bytes_per_step": alg},
+                   "algorithmic_bytes_per_step": alg, "input_sha256": input_sha256(d, torch)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us": round(kern_ms * 1e3, 3),

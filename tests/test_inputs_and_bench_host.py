@@ -122,3 +122,23 @@ def test_cpu_figures_cover_every_row_and_agree_in_units():
         assert abs(gbs - r["value"]) <= 1e-3 * gbs + 1e-4
     assert 1 <= many["threads"] <= 16
     assert "32 rows" in one["sample"] or "(32 rows)" in one["sample"]
+
+
+def test_input_hash_is_reproducible_and_covers_every_tensor():
+    import torch
+
+    import bench
+    from all_reduce_rmsnorm_amd import synth
+
+    w = synth.WORKLOADS["decode_p4_32x7168"]
+    a, b = synth.make_inputs(w), synth.make_inputs(w)
+    assert bench.input_sha256(a, torch) == bench.input_sha256(b, torch)
+    assert bench.input_sha256(synth.make_inputs(w, seed=1), torch) != bench.input_sha256(a, torch)
+    for key in ("residual", "gamma"):
+        c = dict(a)
+        c[key] = a[key].clone()
+        c[key].view(-1)[-1] += 1
+        assert bench.input_sha256(c, torch) != bench.input_sha256(a, torch), key
+    c = dict(a)
+    c["inputs"] = [a["inputs"][1], a["inputs"][0]] + a["inputs"][2:]
+    assert bench.input_sha256(c, torch) != bench.input_sha256(a, torch)
