@@ -5,6 +5,8 @@ Comparison rules (the parity bar):
   * fp32 scales: relative difference <= 1e-5.
   * fp8 e4m3fn codes: within one step in the ordered code sequence
     (sign-magnitude mapped to a signed integer, +0 == -0); NaN codes never.
+  * e5m2 codes: the same, with no inf or NaN code.
+  * MXFP8: see ``check_mx``.
 """
 from __future__ import annotations
 
@@ -44,3 +46,47 @@ def assert_bits_equal(got: np.ndarray, want: np.ndarray, what="bf16"):
     assert got.shape == want.shape, (got.shape, want.shape)
     bad = got != want
     assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} elements differ (first at {np.argwhere(bad)[0].tolist()})"
+
+
+def _bf16_bits(t):
+    from all_reduce_rmsnorm_amd import synth
+
+    return synth.bf16_bits(t)
+
+
+def assert_e5m2_close(got, want, min_exact=0.999):
+    assert not np.any((got & 0x7C) == 0x7C), "e5m2: inf or NaN code in the output"
+    d = np.abs(ordered_fp8(got) - ordered_fp8(want))
+    assert int(d.max()) <= 1, f"e5m2: {int((d > 1).sum())} codes off by more than one step"
+    assert float((d == 0).mean()) >= min_exact
+
+
+def check_mx(orc, xs, res, gamma, out, bscales, res_out, eps=1e-6, woff=0.0, min_exact=None):
+    """MXFP8 outputs against the oracle: E8M0 exponents equal except in blocks
+    whose largest magnitude lies within fp32 rounding of a power of two (either
+    neighbour is then correct, and the codes are checked for the GPU's
+    exponent); codes within one e4m3fn step."""
+    q, bs, h = orc.arnfp8_mx([_bf16_bits(x) for x in xs], _bf16_bits(gamma), eps, woff,
+                             residual_in=None if res is None else _bf16_bits(res))
+    if res_out is not None:
+        assert_bits_equal(_bf16_bits(res_out), h, "residual_out")
+    got_q = out.cpu().numpy()
+    got_b = bscales.cpu().numpy()
+    rows, cols = got_q.shape
+    mism = np.argwhere(got_b != bs)
+    if len(mism):
+        y = orc.norm_rows([_bf16_bits(x) for x in xs], _bf16_bits(gamma), eps, woff,
+                          residual_in=None if res is None else _bf16_bits(res))
+        for i, b in mism:
+            blk = y[i, 32 * b: 32 * b + 32]
+            amax = np.max(np.abs(blk))
+            frac = amax / 2.0 ** np.floor(np.log2(amax)) if amax > 0 else 1.5
+            near_pow2 = min(frac - 1.0, 2.0 - frac) < 2.0 ** -20
+            assert near_pow2 and abs(int(got_b[i, b]) - int(bs[i, b])) == 1, (
+                f"block ({i},{b}): exponent {int(got_b[i, b]) - 127} vs oracle {int(bs[i, b]) - 127}, "
+                f"amax {amax!r}")
+            q[i, 32 * b: 32 * b + 32] = orc.mx_quantize_block(blk, int(got_b[i, b]) - 127)
+    assert len(mism) <= max(1, got_b.size // 10000)
+    if min_exact is None:
+        min_exact = 0.99 if rows * cols < 4096 else 0.999
+    assert_fp8_close(got_q, q, min_exact=min_exact, what="mxfp8")

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests._util import assert_bits_equal, assert_fp8_close, assert_scales_close, ordered_fp8
+from tests._util import assert_bits_equal, assert_e5m2_close, assert_fp8_close, assert_scales_close, check_mx
 
 pytestmark = pytest.mark.gpu
 
@@ -41,13 +41,6 @@ def _case(seed, rows, cols, P, std=0.5):
     res = torch.randn((rows, cols), generator=g).to(torch.bfloat16)
     gamma = (torch.rand((cols,), generator=g) * 0.4 + 0.8).to(torch.bfloat16)
     return xs, res, gamma
-
-
-def assert_e5m2_close(got, want, min_exact=0.999):
-    assert not np.any((got & 0x7C) == 0x7C), "e5m2: inf or NaN code in the output"
-    d = np.abs(ordered_fp8(got) - ordered_fp8(want))
-    assert int(d.max()) <= 1, f"e5m2: {int((d > 1).sum())} codes off by more than one step"
-    assert float((d == 0).mean()) >= min_exact
 
 
 @pytest.mark.parametrize("rows,cols,P", [(4, 256, 2), (32, 7168, 4), (37, 7176, 8), (3, 65536, 3)])
@@ -81,31 +74,6 @@ def test_e5m2_clamp_and_floor(arn, orc):
     assert np.all(sg[:7] == np.float32(2.0 / 57344.0)) and np.all(s[:7] == sg[:7])
     assert sg[7] == np.float32(1.0 / (57344.0 * 512.0)) == s[7]
     assert_e5m2_close(out.cpu().numpy(), q, min_exact=0.99)
-
-
-def check_mx(orc, xs, res, gamma, out, bscales, res_out, eps=1e-6, woff=0.0):
-    q, bs, h = orc.arnfp8_mx([_bits(x) for x in xs], _bits(gamma), eps, woff,
-                             residual_in=None if res is None else _bits(res))
-    if res_out is not None:
-        assert_bits_equal(_bits(res_out), h, "residual_out")
-    got_q = out.cpu().numpy()
-    got_b = bscales.cpu().numpy()
-    rows, cols = got_q.shape
-    mism = np.argwhere(got_b != bs)
-    if len(mism):
-        y = orc.norm_rows([_bits(x) for x in xs], _bits(gamma), eps, woff,
-                          residual_in=None if res is None else _bits(res))
-        for i, b in mism:
-            blk = y[i, 32 * b: 32 * b + 32]
-            amax = np.max(np.abs(blk))
-            frac = amax / 2.0 ** np.floor(np.log2(amax)) if amax > 0 else 1.5
-            near_pow2 = min(frac - 1.0, 2.0 - frac) < 2.0 ** -20
-            assert near_pow2 and abs(int(got_b[i, b]) - int(bs[i, b])) == 1, (
-                f"block ({i},{b}): exponent {int(got_b[i, b]) - 127} vs oracle {int(bs[i, b]) - 127}, "
-                f"amax {amax!r}")
-            q[i, 32 * b: 32 * b + 32] = orc.mx_quantize_block(blk, int(got_b[i, b]) - 127)
-    assert len(mism) <= max(1, got_b.size // 10000)
-    assert_fp8_close(got_q, q, min_exact=0.99 if rows * cols < 4096 else 0.999, what="mxfp8")
 
 
 @pytest.mark.parametrize("rows,cols,P", [(4, 256, 2), (32, 7168, 4), (37, 2880, 8), (128, 8192, 8),
