@@ -25,7 +25,7 @@
 //  * fl32(h * g) stays in registers between the statistics pass and the
 //    quantisation pass: the only global traffic is the algorithmic one.
 //  * (sum h^2, max |h g|) are reduced across the wave with DPP moves inside
-//    each row of 16 lanes and two lane exchanges across rows, then across
+//    each row of 16 lanes and two lane-swap moves across rows, then across
 //    waves through LDS with one barrier per row; the LDS slot alternates with
 //    the row parity so consecutive rows need no second barrier.
 //  * fp8 values come from the packed OCP e4m3fn / e5m2 conversions after an
@@ -188,28 +188,50 @@ __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false));
 }
 
+// Pairs across rows with gfx950's lane-swap moves (VALU, no LDS round trip).
+// Given the same value twice, v_permlane16_swap returns, at every lane, the
+// values of lanes l and l ^ 16 (one in each result), and v_permlane32_swap
+// those of lanes l and l ^ 32.  Both partners combine the same two values
+// (the operations below commute), so they agree bit for bit.
+__device__ __forceinline__ f32x2 pair16(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  // Elements are read into scalars first: a bit cast of a vector element
+  // expression would read element 0 whatever the index.
+  const uint32_t a = s[0], b = s[1];
+  return (f32x2){__uint_as_float(a), __uint_as_float(b)};
+}
+__device__ __forceinline__ f32x2 pair32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto s = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t a = s[0], b = s[1];
+  return (f32x2){__uint_as_float(a), __uint_as_float(b)};
+}
+
 // Reductions across the 64 lanes of a wave; every lane gets the result.
 // Within a row of 16 lanes: xor 1, xor 2 (the quad), then the 8-lane and
 // 16-lane mirrors, which pair each lane with one in the other half; across
-// rows: lane exchanges at distance 16 and 32.  The order of the additions
-// is fixed, so the sum is deterministic.
+// rows: the pairs at distance 16, then 32.  The order of the additions is
+// fixed, so the sum is deterministic.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<kDppQuadXor1>(v);
   v += dpp<kDppQuadXor2>(v);
   v += dpp<kDppHalfMirror>(v);
   v += dpp<kDppMirror>(v);
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  f32x2 p = pair16(v);
+  v = p.x + p.y;
+  p = pair32(v);
+  return p.x + p.y;
 }
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<kDppQuadXor1>(v));
   v = fmaxf(v, dpp<kDppQuadXor2>(v));
   v = fmaxf(v, dpp<kDppHalfMirror>(v));
   v = fmaxf(v, dpp<kDppMirror>(v));
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  f32x2 p = pair16(v);
+  v = fmaxf(p.x, p.y);
+  p = pair32(v);
+  return fmaxf(p.x, p.y);
 }
 
 // ---------------------------------------------------------------- kernels --
