@@ -150,3 +150,42 @@ def test_every_format_under_both_store_policies(arn, orc, fmt, stores):
         assert_fp8_close(out.cpu().numpy(), q)
     else:
         assert_e5m2_close(out.cpu().numpy(), q)
+
+
+@pytest.mark.parametrize("fmt", ["e5m2", "mxfp8"])
+def test_formats_on_the_full_prefill_workload_sampled_rows(arn, orc, fmt):
+    """Each alternative format on the full prefill workload (8192 x 7168, P = 8,
+    residual out of place, the launch the benchmark times); the oracle checks
+    a seeded sample of rows."""
+    from all_reduce_rmsnorm_amd import synth
+
+    w = synth.WORKLOADS["prefill_p8_8192x7168"]
+    print(f"[{fmt}] workload {w.name} (sampled rows)", flush=True)
+    d = synth.make_inputs(w, device=DEV)
+    out = torch.empty((w.rows, w.cols), dtype=torch.uint8, device=DEV)
+    res_out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=DEV)
+    if fmt == "mxfp8":
+        scales = torch.empty((w.rows, w.cols // 32), dtype=torch.uint8, device=DEV)
+        code = arn.FMT_MXFP8
+    else:
+        scales = torch.empty((w.rows,), dtype=torch.float32, device=DEV)
+        code = arn.FMT_E5M2
+    arn.arnfp8_run_fmt(d["inputs"], d["residual"], res_out, out, scales, d["gamma"], w.eps,
+                       w.weight_offset, w.scale_ub, out_format=code)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, w.rows - 1], rng.choice(w.rows, 126, replace=False)]))
+    idx = torch.from_numpy(rows).to(DEV)
+    xs_h = [x.index_select(0, idx).cpu() for x in d["inputs"]]
+    res_h = d["residual"].index_select(0, idx).cpu()
+    gamma_h = d["gamma"].cpu()
+    if fmt == "mxfp8":
+        check_mx(orc, xs_h, res_h, gamma_h, out.index_select(0, idx), scales.index_select(0, idx),
+                 res_out.index_select(0, idx), eps=w.eps, woff=w.weight_offset)
+        return
+    q, s, h = orc.arnfp8_e5m2([_bits(x) for x in xs_h], _bits(gamma_h), w.eps, w.weight_offset,
+                              w.scale_ub, residual_in=_bits(res_h))
+    assert_bits_equal(_bits(res_out.index_select(0, idx)), h, "residual_out")
+    assert_scales_close(scales.index_select(0, idx).cpu().numpy(), s)
+    assert_e5m2_close(out.index_select(0, idx).cpu().numpy(), q)
+
