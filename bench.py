@@ -613,6 +613,12 @@ def main():
                 cold[name] = round(us, 3)
         result["latency_us_per_call_cold"] = cold
         log(f"bench: graph-replayed latency, inputs not in cache {cold}")
+        # The same figures as algorithmic bytes per second (latency-bound
+        # shapes: these are far below the HBM peak by nature).
+        result["latency_gbs"] = {
+            kind: {n: round(synth.WORKLOADS[n].algorithmic_bytes() / (us * 1e-6) / 1e9, 1)
+                   for n, us in table.items()}
+            for kind, table in (("warm", lat), ("cold", cold))}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, d, torch)
         log(f"bench: cpu baseline {result['cpu_baseline']}")
