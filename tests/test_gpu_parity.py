@@ -494,3 +494,45 @@ def test_graph_replay_of_share_and_formats(arn, synth):
         torch.cuda.synchronize()
         for a, b in zip((stg, q5, s5, qm, sm, ro), eager):
             assert torch.equal(a, b), k
+
+
+def test_concurrent_calls_on_two_streams(arn, synth):
+    """The library keeps no state between calls: two streams running the fused
+    op at the same time, each on its own buffers, give the single-stream
+    results bit for bit."""
+    w = synth.WORKLOADS["unit_offset_p8_128x8192"]
+    print("[fused] two streams", flush=True)
+    sets = []
+    for seed in (3, 4):
+        d = synth.make_inputs(w, device=DEV, seed=seed)
+        out = torch.empty((w.rows, w.cols), dtype=torch.float8_e4m3fn, device=DEV)
+        sc = torch.empty((w.rows,), dtype=torch.float32, device=DEV)
+        ro = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=DEV)
+        sets.append((d, out, sc, ro))
+
+    def call(k):
+        d, out, sc, ro = sets[k]
+        arn.arnfp8_run(d["inputs"], d["residual"], ro, out, sc, d["gamma"], w.eps,
+                       w.weight_offset, w.scale_ub)
+
+    ref = []
+    for k in range(2):
+        call(k)
+        torch.cuda.synchronize()
+        ref.append([t.clone() for t in sets[k][1:]])
+        for t in sets[k][1:]:
+            t.zero_()
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(20):
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                call(k)
+    for s in streams:
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for k in range(2):
+        for got, want in zip(sets[k][1:], ref[k]):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), k
