@@ -1,8 +1,11 @@
 """Thin Python binding of ``libarnfp8.so``, the gfx950 fused all-reduce epilogue.
 
 Every entry point here has the C ABI's name and argument order and does only
-argument marshalling: tensors become device pointers, the stream becomes the
-current PyTorch stream's handle, and a non-zero status raises ``ArnFp8Error``.
+argument marshalling: tensors are checked to be dense device memory of the
+declared element type and of the size the call's shape implies (the library
+sees bare pointers and cannot), then become device pointers; the stream
+becomes the current PyTorch stream's handle; a non-zero status raises
+``ArnFp8Error``.
 All arithmetic runs in the library's HIP kernels; there is no CPU fallback --
 if the library is not built, every call raises.
 
@@ -112,12 +115,13 @@ _F32 = ("float32",)
 _U8 = ("uint8", "int8")
 
 
-def _ptr(t, kinds=None, what="tensor"):
-    """Device pointer of a tensor (or a raw integer address, or None).
+def _ptr(t, kinds=None, what="tensor", nbytes=None):
+    """Address of a tensor's data (or a raw integer address, or None).
 
-    Tensors must be dense (contiguous) and, when ``kinds`` is given, of one of
-    those dtypes, and on the device: the library reads plain row-major device
-    memory.
+    Tensors must be dense (contiguous), of one of the dtypes in ``kinds`` when
+    it is given, and hold at least ``nbytes`` bytes when that is positive: the
+    library reads and writes plain row-major memory of the sizes the call's
+    shape implies.  ``_on_device`` checks where they live.
     """
     if t is None:
         return None
@@ -127,14 +131,27 @@ def _ptr(t, kinds=None, what="tensor"):
         raise ValueError(f"{what} must be contiguous (the library reads dense row-major memory)")
     if kinds is not None and str(t.dtype).replace("torch.", "") not in kinds:
         raise TypeError(f"{what} has dtype {t.dtype}; expected one of {', '.join(kinds)}")
-    if t.device.type != "cuda":
-        raise ValueError(f"{what} must be a device (cuda) tensor, got {t.device}")
+    if nbytes is not None and nbytes > 0 and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what} holds {t.numel() * t.element_size()} bytes; the call's shape "
+                         f"needs {nbytes}")
     return t.data_ptr()
 
 
-def _ptr_array(inputs):
-    ptrs = [_ptr(x, _BF16, f"inputs[{i}]") for i, x in enumerate(inputs)]
+def _ptr_array(inputs, nbytes=None):
+    ptrs = [_ptr(x, _BF16, f"inputs[{i}]", nbytes) for i, x in enumerate(inputs)]
     return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+
+
+def _on_device(**tensors):
+    """Every tensor argument (lists included) must be device memory."""
+    for what, t in tensors.items():
+        items = list(enumerate(t)) if isinstance(t, (list, tuple)) else [(None, t)]
+        for i, x in items:
+            if x is None or isinstance(x, int):
+                continue
+            if x.device.type != "cuda":
+                name = what if i is None else f"{what}[{i}]"
+                raise ValueError(f"{name} must be a device (cuda) tensor, got {x.device}")
 
 
 def _stream(stream):
@@ -174,12 +191,14 @@ def arnfp8_run(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps, w
     Runs on ``stream`` (default: PyTorch's current stream).
     """
     rows, cols, P = _shape(inputs, rows, cols, P)
-    st = library().arnfp8_run(_ptr_array(inputs), _ptr(residual_in, _BF16, "residual_in"),
-                              _ptr(residual_out, _BF16, "residual_out"),
-                              _ptr(out_fp8, _FP8, "out_fp8"), _ptr(scales, _F32, "scales"),
-                              _ptr(gamma, _BF16, "gamma"), float(eps),
-                              float(weight_offset), float(scale_ub), rows, cols, P,
-                              _stream(stream))
+    n = rows * cols
+    ptrs = (_ptr_array(inputs, 2 * n), _ptr(residual_in, _BF16, "residual_in", 2 * n),
+            _ptr(residual_out, _BF16, "residual_out", 2 * n), _ptr(out_fp8, _FP8, "out_fp8", n),
+            _ptr(scales, _F32, "scales", 4 * rows), _ptr(gamma, _BF16, "gamma", 2 * cols))
+    _on_device(inputs=inputs, residual_in=residual_in, residual_out=residual_out,
+               out_fp8=out_fp8, scales=scales, gamma=gamma)
+    st = library().arnfp8_run(*ptrs, float(eps), float(weight_offset), float(scale_ub), rows,
+                              cols, P, _stream(stream))
     if st != 0:
         raise ArnFp8Error("arnfp8_run", st)
 
@@ -192,12 +211,14 @@ def arnfp8_run_ex(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps
     if isinstance(launch, dict):
         launch = Launch(**launch)
     opt = ctypes.byref(launch) if launch is not None else None
-    st = library().arnfp8_run_ex(_ptr_array(inputs), _ptr(residual_in, _BF16, "residual_in"),
-                                 _ptr(residual_out, _BF16, "residual_out"),
-                                 _ptr(out_fp8, _FP8, "out_fp8"), _ptr(scales, _F32, "scales"),
-                                 _ptr(gamma, _BF16, "gamma"), float(eps),
-                                 float(weight_offset), float(scale_ub), rows, cols, P,
-                                 _stream(stream), opt)
+    n = rows * cols
+    ptrs = (_ptr_array(inputs, 2 * n), _ptr(residual_in, _BF16, "residual_in", 2 * n),
+            _ptr(residual_out, _BF16, "residual_out", 2 * n), _ptr(out_fp8, _FP8, "out_fp8", n),
+            _ptr(scales, _F32, "scales", 4 * rows), _ptr(gamma, _BF16, "gamma", 2 * cols))
+    _on_device(inputs=inputs, residual_in=residual_in, residual_out=residual_out,
+               out_fp8=out_fp8, scales=scales, gamma=gamma)
+    st = library().arnfp8_run_ex(*ptrs, float(eps), float(weight_offset), float(scale_ub), rows,
+                                 cols, P, _stream(stream), opt)
     if st != 0:
         raise ArnFp8Error("arnfp8_run_ex", st)
 
@@ -205,8 +226,10 @@ def arnfp8_run_ex(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps
 def arn_sum_bf16(inputs, out, rows=None, cols=None, P=None, stream=None) -> None:
     """Rank-order fp32 sum of P bf16 slabs, rounded once to bf16, into ``out``."""
     rows, cols, P = _shape(inputs, rows, cols, P)
-    st = library().arn_sum_bf16(_ptr_array(inputs), _ptr(out, _BF16, "out"), rows, cols, P,
-                                _stream(stream))
+    n = rows * cols
+    ptrs = (_ptr_array(inputs, 2 * n), _ptr(out, _BF16, "out", 2 * n))
+    _on_device(inputs=inputs, out=out)
+    st = library().arn_sum_bf16(*ptrs, rows, cols, P, _stream(stream))
     if st != 0:
         raise ArnFp8Error("arn_sum_bf16", st)
 
@@ -220,12 +243,15 @@ def arnfp8_run_share(inputs, residual_in, residual_out, staging, gamma, eps, wei
                      scale_ub, rows=None, cols=None, P=None, ngpus=1, rank=0, stream=None) -> None:
     """The fused epilogue on rank ``rank``'s row share, fp8 rows + scales into ``staging``."""
     rows, cols, P = _shape(inputs, rows, cols, P)
-    st = library().arnfp8_run_share(_ptr_array(inputs), _ptr(residual_in, _BF16, "residual_in"),
-                                    _ptr(residual_out, _BF16, "residual_out"),
-                                    _ptr(staging, _U8, "staging"), _ptr(gamma, _BF16, "gamma"),
-                                    float(eps), float(weight_offset),
-                                    float(scale_ub), rows, cols, P, int(ngpus), int(rank),
-                                    _stream(stream))
+    n = rows * cols
+    slot = arnfp8_stage_bytes(rows, cols, ngpus) if rows >= 0 and cols > 0 and ngpus >= 1 else None
+    ptrs = (_ptr_array(inputs, 2 * n), _ptr(residual_in, _BF16, "residual_in", 2 * n),
+            _ptr(residual_out, _BF16, "residual_out", 2 * n), _ptr(staging, _U8, "staging", slot),
+            _ptr(gamma, _BF16, "gamma", 2 * cols))
+    _on_device(inputs=inputs, residual_in=residual_in, residual_out=residual_out,
+               staging=staging, gamma=gamma)
+    st = library().arnfp8_run_share(*ptrs, float(eps), float(weight_offset), float(scale_ub),
+                                    rows, cols, P, int(ngpus), int(rank), _stream(stream))
     if st != 0:
         raise ArnFp8Error("arnfp8_run_share", st)
 
@@ -242,13 +268,16 @@ def arnfp8_run_fmt(inputs, residual_in, residual_out, out_fp8, scales, gamma, ep
     opt = ctypes.byref(launch) if launch is not None else None
     # an unknown format is left to the library, which reports it as BAD_FORMAT
     scale_kinds = {FMT_MXFP8: _U8, FMT_E4M3FN: _F32, FMT_E5M2: _F32}.get(int(out_format))
-    st = library().arnfp8_run_fmt(_ptr_array(inputs), _ptr(residual_in, _BF16, "residual_in"),
-                                  _ptr(residual_out, _BF16, "residual_out"),
-                                  _ptr(out_fp8, _FP8, "out_fp8"),
-                                  _ptr(scales, scale_kinds, "scales"), _ptr(gamma, _BF16, "gamma"),
-                                  float(eps),
-                                  float(weight_offset), float(scale_ub), rows, cols, P,
-                                  int(out_format), _stream(stream), opt)
+    n = rows * cols
+    scale_bytes = {FMT_MXFP8: rows * (cols // 32), FMT_E4M3FN: 4 * rows,
+                   FMT_E5M2: 4 * rows}.get(int(out_format))
+    ptrs = (_ptr_array(inputs, 2 * n), _ptr(residual_in, _BF16, "residual_in", 2 * n),
+            _ptr(residual_out, _BF16, "residual_out", 2 * n), _ptr(out_fp8, _FP8, "out_fp8", n),
+            _ptr(scales, scale_kinds, "scales", scale_bytes), _ptr(gamma, _BF16, "gamma", 2 * cols))
+    _on_device(inputs=inputs, residual_in=residual_in, residual_out=residual_out,
+               out_fp8=out_fp8, scales=scales, gamma=gamma)
+    st = library().arnfp8_run_fmt(*ptrs, float(eps), float(weight_offset), float(scale_ub), rows,
+                                  cols, P, int(out_format), _stream(stream), opt)
     if st != 0:
         raise ArnFp8Error("arnfp8_run_fmt", st)
 
@@ -258,7 +287,9 @@ def arnfp8_convert_f32(inp, out, fmt, n=None, stream=None) -> None:
     ``fmt`` (FMT_E4M3FN, FMT_E5M2: clamped; CVT_BF16), round to nearest even."""
     n = int(inp.numel()) if n is None else int(n)
     out_kinds = ("bfloat16", "int16", "uint16") if int(fmt) == CVT_BF16 else _FP8
-    st = library().arnfp8_convert_f32(_ptr(inp, _F32, "inp"), _ptr(out, out_kinds, "out"), n,
-                                      int(fmt), _stream(stream))
+    out_bytes = n * (2 if int(fmt) == CVT_BF16 else 1)
+    ptrs = (_ptr(inp, _F32, "inp", 4 * n), _ptr(out, out_kinds, "out", out_bytes))
+    _on_device(inp=inp, out=out)
+    st = library().arnfp8_convert_f32(*ptrs, n, int(fmt), _stream(stream))
     if st != 0:
         raise ArnFp8Error("arnfp8_convert_f32", st)

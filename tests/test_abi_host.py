@@ -236,3 +236,40 @@ def test_binding_refuses_what_the_library_cannot_read():
         arn._ptr(s.double(), arn._F32, "scales")
     with pytest.raises(ValueError, match="device"):
         arn.arnfp8_run([x], None, None, out, s, g, 1e-6, 0.0, 1.0)
+
+
+def test_binding_refuses_buffers_smaller_than_the_shape():
+    import torch
+
+    import all_reduce_rmsnorm_amd as arn
+
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    out = torch.zeros((4, 64), dtype=torch.uint8)
+    s = torch.zeros((4,), dtype=torch.float32)
+    g = torch.zeros((64,), dtype=torch.bfloat16)
+    cases = [
+        ("out_fp8", dict(out_fp8=out[:3])),
+        ("scales", dict(scales=s[:3])),
+        ("gamma", dict(gamma=g[:56])),
+        ("residual_out", dict(residual_out=x[:3])),
+        ("inputs[1]", dict(inputs=[x, x[:2]])),
+    ]
+    for what, change in cases:
+        args = dict(inputs=[x], residual_in=None, residual_out=None, out_fp8=out, scales=s,
+                    gamma=g)
+        args.update(change)
+        with pytest.raises(ValueError, match=r"\b" + what.replace("[", r"\[").replace("]", r"\]")
+                           + " holds"):
+            arn.arnfp8_run(args["inputs"], args["residual_in"], args["residual_out"],
+                           args["out_fp8"], args["scales"], args["gamma"], 1e-6, 0.0, 1.0,
+                           rows=4, cols=64)
+    mx = torch.zeros((4, 1), dtype=torch.uint8)  # needs 4 x (64 / 32) bytes
+    with pytest.raises(ValueError, match="scales holds"):
+        arn.arnfp8_run_fmt([x], None, None, out, mx, g, 1e-6, 0.0, 1.0, out_format=arn.FMT_MXFP8)
+    with pytest.raises(ValueError, match="out holds"):
+        arn.arn_sum_bf16([x], x[:2])
+    with pytest.raises(ValueError, match="staging holds"):
+        arn.arnfp8_run_share([x], None, None, torch.zeros(8, dtype=torch.uint8), g, 1e-6, 0.0,
+                             1.0, ngpus=2, rank=0)
+    with pytest.raises(ValueError, match="out holds"):
+        arn.arnfp8_convert_f32(torch.zeros(16), torch.zeros(8, dtype=torch.uint8), arn.FMT_E4M3FN)
