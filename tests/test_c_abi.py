@@ -27,3 +27,12 @@ def test_header_compiles_as_c99_and_validation_codes_hold(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "abi_check: ok" in r.stdout
+
+
+def test_gpu_round_trip_program_builds(tmp_path):
+    """The plain-C GPU round trip (run by the GPU suite) compiles and links
+    here too, with gcc -Werror."""
+    from tests.test_gpu_c_roundtrip import build_roundtrip
+
+    build_roundtrip(tmp_path / "gpu_roundtrip")
+    assert (tmp_path / "gpu_roundtrip").exists()
