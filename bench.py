@@ -558,6 +558,23 @@ def main():
             fmt_out[f"{name}_us_per_call"] = round(f_k * 1e3, 2)
         result["formats"] = fmt_out
         del mx_scales
+        # The residual updated in place (residual_out == residual_in), as a
+        # transformer's residual stream is: each output set carries its own
+        # residual copy, so the rotation still keeps every call out of cache.
+        if d["residual"] is not None:
+            res_sets = [d["residual"].clone() for _ in d["outs"]]
+
+            def in_place_one(o, r):
+                return lambda: arn.arnfp8_run(d["inputs"], r, r, o["out"], o["scales"], d["gamma"],
+                                              w.eps, w.weight_offset, w.scale_ub)
+            _, ip_k = time_steps(torch, rotating([in_place_one(o, r) for o, r in
+                                                  zip(d["outs"], res_sets)]),
+                                 max(10, args.steps // 2), 3)
+            result["in_place_residual"] = {
+                "us_per_call": round(ip_k * 1e3, 2),
+                "gbs": round(alg / (ip_k * 1e-3) / 1e9, 1),
+            }
+            del res_sets
         # One rank's share of the two-stage layout (8 ranks): the single-GPU
         # half of the large-payload path, at its real shape.
         ngpus = 8
