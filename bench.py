@@ -49,11 +49,12 @@ DECODE_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "tiny_p2_4x2
                     "sum_p4_64x4096"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
 # The device code, the host code that picks its launch shape and cache
-# policy, and the build flags: the committed HBM-counter summary applies only
-# while these are unchanged.
+# policy, the ABI header whose constants both use, and the build flags: the
+# committed HBM-counter summary applies only while these are unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_kernels.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_tables.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8.hip"),
+                  os.path.join(ROOT, "include", "arnfp8.h"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
 
 

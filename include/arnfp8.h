@@ -31,8 +31,9 @@
  *     and its P pointers are passed by value to the kernel; the caller may
  *     reuse the array as soon as the call returns.
  *   - Ownership: the caller owns every buffer.  The library allocates nothing
- *     and keeps no state between calls, so calls may be captured in a HIP
- *     graph; pointers captured that way must stay valid for the graph's life.
+ *     and keeps no state between calls (beyond a cached compute-unit count per
+ *     device), so calls may be captured in a HIP graph; pointers captured that
+ *     way must stay valid for the graph's life.
  *   - Validation happens on the host before any launch and touches no device
  *     state; a call that returns an error has launched nothing.
  *   - Execution is asynchronous on `stream` (NULL = the default stream);
@@ -65,7 +66,7 @@ extern "C" {
 #define ARNFP8_BAD_P 4        /* P outside [1, ARNFP8_MAX_P]                     */
 #define ARNFP8_ALIAS 5        /* an output overlaps an input or another output
                                  (residual_out == residual_in is allowed)      */
-#define ARNFP8_HIP_ERROR 6    /* the launch failed (hipGetLastError)             */
+#define ARNFP8_HIP_ERROR 6    /* the kernel launch call itself failed            */
 #define ARNFP8_BAD_CONFIG 7   /* an arnfp8_run_ex launch option is invalid       */
 #define ARNFP8_BAD_SHARE 8    /* ngpus < 1, or rank outside [0, ngpus)           */
 #define ARNFP8_BAD_FORMAT 9   /* unknown out_format                              */
@@ -111,7 +112,8 @@ int arnfp8_run(const void *const *inputs, const void *residual_in, void *residua
 #define ARNFP8_STORES_SC1 2  /* device-scope coherent (sc1) stores           */
 
 /* Launch options for arnfp8_run_ex / arnfp8_run_fmt.  Zero in any field means
- * "automatic".  No option changes any result. */
+ * "automatic".  No option changes a bf16 result (see arnfp8_run_ex for the
+ * last bits of scales and fp8 codes). */
 typedef struct arnfp8_launch {
   int variant; /* ARNFP8_VARIANT_*                                               */
   int threads; /* lanes per workgroup: a multiple of 64 in [64, 512], or up to
