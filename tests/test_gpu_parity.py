@@ -96,6 +96,24 @@ def test_sum_workload_full_size(arn, orc, synth):
     assert_bits_equal(_bits(out), orc.sum_bf16([_bits(x) for x in h["inputs"]]), "sum")
 
 
+@pytest.mark.parametrize("P", [3, 8])
+def test_sum_wide_path_ragged_tail(arn, orc, P):
+    """The large-tensor path of the sum (4 chunks per lane, a buffer window per
+    iteration) on a tensor whose chunk count is not a multiple of the window:
+    9001 x 7176 has 8,073,897 chunks.  Every element is compared, and bytes
+    past the end of the output stay untouched."""
+    rows, cols = 9001, 7176
+    print(f"[sum] wide ragged P={P} rows={rows} cols={cols}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(77 + P)
+    xs = [torch.randn((rows, cols), generator=g, device=DEV, dtype=torch.bfloat16) for _ in range(P)]
+    guard = torch.full((rows * cols + 4096,), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = guard[: rows * cols].view(rows, cols)
+    arn.arn_sum_bf16(xs, out)
+    torch.cuda.synchronize()
+    assert_bits_equal(_bits(out), orc.sum_bf16([_bits(x) for x in xs]), "sum")
+    assert torch.all(guard[rows * cols:] == -7.0)
+
+
 def test_sum_negative_zero_and_ties(arn, orc):
     # P = 1 keeps -0; exact half-ulp ties round to even.
     vals = torch.tensor([[-0.0, 0.0, 16.0, 16.125, 1.0, -16.0, 8.0, 3.0]], dtype=torch.float32)
