@@ -372,6 +372,11 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
   int parity = 0;
 
   for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x, parity ^= 1) {
+    // Wave priority: low while the row's loads are issued, high once they are
+    // in flight (the reduction, quantisation and stores).  Measured on MI355X:
+    // decode (P = 4, 32 x 7168) 3.62 against 3.68 us per call; prefill
+    // unchanged; the opposite order costs prefill 1 %.
+    __builtin_amdgcn_s_setprio(0);
     // Row-uniform bases (scalar registers); lanes add a 32-bit chunk index.
     const int64_t base = row * (int64_t)a.c16;
     const u32x4 *xs[P];
@@ -400,6 +405,7 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
         if constexpr (RES_IN) r[k] = load16(rin + c);
         g[k] = a.gamma[c];
       }
+      if (v0 == 0) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
       for (int k = 0; k < G; ++k) {
         const int v = v0 + k;
