@@ -178,7 +178,7 @@ int prepare_fused(const void *const *inputs, const void *residual_in, void *resi
   a->eps = eps;
   a->woff = weight_offset;
   a->ub = scale_ub;
-  a->cols_f = (float)cols;
+  a->inv_cols = 1.0f / (float)cols;
   a->rows = rows;
   a->c16 = (int)(cols / 8);
   return ARNFP8_OK;

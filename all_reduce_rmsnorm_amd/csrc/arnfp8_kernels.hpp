@@ -327,7 +327,7 @@ struct RowArgs {
   uint8_t *mx_scales;  // MXFP8: E8M0 [rows, c16 / 4]
   const u32x4 *gamma;
   float eps, woff, ub;
-  float cols_f;
+  float inv_cols;  // fl32(1 / cols)
   int64_t rows;
   int c16;  // 16-byte chunks per row
 };
@@ -450,12 +450,17 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
       m = fmaxf(m, red[parity][w][1]);
     }
 
-    const float r = 1.0f / sqrtf(tot / a.cols_f + a.eps);
+    // The row scalars sit on every row's critical path, so r and 1/scale use
+    // the hardware reciprocal square root and reciprocal (each within 1 ulp;
+    // measured: decode 3.49 against 3.61 us per call with the IEEE square root
+    // and divisions).  The division by the format maximum stays IEEE, so a
+    // clamped scale is exactly fl32(scale_ub / fmax).
+    const float r = __builtin_amdgcn_rsqf(tot * a.inv_cols + a.eps);
     float cq = 0.0f;
     if constexpr (FMT != kFmtMx) {
       const float amax = m * r;
       const float scale = fmaxf(fminf(amax, a.ub) / fmt_max<FMT>(), fmt_floor<FMT>());
-      cq = r / scale;
+      cq = r * __builtin_amdgcn_rcpf(scale);
       if (t == 0) a.scales[row] = scale;
     }
 

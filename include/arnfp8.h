@@ -92,7 +92,11 @@ extern "C" {
  * scales       device fp32 [rows] (the [rows, 1] per-row scales)
  * gamma        device bf16 [cols]
  * eps, weight_offset, scale_ub   fp32 scalars, used as given
- * Norm and scale arithmetic is fp32 with IEEE division and square root.
+ * Norm and scale arithmetic is fp32.  r comes from the hardware reciprocal
+ * square root of fl32(sum_j h_j^2 * fl32(1 / cols)) + eps, and 1 / scale from
+ * the hardware reciprocal (each within 1 ulp); the division by 448 is IEEE, so
+ * a clamped scale is exactly fl32(scale_ub / 448).  Scales agree with the
+ * exact definition to within a few fp32 ulps.
  */
 int arnfp8_run(const void *const *inputs, const void *residual_in, void *residual_out,
                void *out_fp8, float *scales, const void *gamma, float eps,
