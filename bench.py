@@ -219,8 +219,9 @@ def cpu_baseline(w, d, torch, min_seconds=10.0, max_passes=3):
 
     block = 1024
     gamma = synth.bf16_bits(d["gamma"])
-    total_t, passes = 0.0, 0
-    while passes < max_passes and (passes == 0 or total_t < min_seconds):
+    times, total_t = [], 0.0
+    while len(times) < max_passes and (not times or total_t < min_seconds):
+        pass_t = 0.0
         for r0 in range(0, w.rows, block):
             r1 = min(w.rows, r0 + block)
             xs = [synth.bf16_bits(x[r0:r1]) for x in d["inputs"]]
@@ -230,18 +231,44 @@ def cpu_baseline(w, d, torch, min_seconds=10.0, max_passes=3):
                 oracle.sum_bf16(xs)
             else:
                 oracle.arnfp8(xs, gamma, w.eps, w.weight_offset, w.scale_ub, residual_in=res)
-            total_t += time.perf_counter() - t
-        passes += 1
-    per_pass = total_t / passes
+            pass_t += time.perf_counter() - t
+        times.append(pass_t)
+        total_t += pass_t
+    per_pass = sorted(times)[len(times) // 2]
     return {
         "value": round(w.algorithmic_bytes() / per_pass / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"every row of {w.name} ({w.rows} rows), {passes} pass(es), "
+        "sample": f"every row of {w.name} ({w.rows} rows), median of {len(times)} pass(es), "
                   f"{per_pass * 1e3:.1f} ms per pass; single-threaded C oracle",
         "ms_per_step": round(per_pass * 1e3, 3),
     }
+
+
+def cpu_oracle_latency(names, runs=20):
+    """Median microseconds per call of the single-threaded oracle on the small
+    workloads (host bytes drawn by the same recipe), next to the GPU's."""
+    import oracle
+    from all_reduce_rmsnorm_amd import synth
+
+    out = {}
+    for name in names:
+        w = synth.WORKLOADS[name]
+        d = synth.make_inputs(w, device="cpu")
+        xs = [synth.bf16_bits(x) for x in d["inputs"]]
+        res = None if d["residual"] is None else synth.bf16_bits(d["residual"])
+        gamma = synth.bf16_bits(d["gamma"])
+        ts = []
+        for _ in range(runs):
+            t = time.perf_counter()
+            if w.sum_only:
+                oracle.sum_bf16(xs)
+            else:
+                oracle.arnfp8(xs, gamma, w.eps, w.weight_offset, w.scale_ub, residual_in=res)
+            ts.append(time.perf_counter() - t)
+        out[name] = round(sorted(ts)[len(ts) // 2] * 1e6, 1)
+    return out
 
 
 def host_cpu():
@@ -642,6 +669,8 @@ def main():
         log(f"bench: cpu baseline {result['cpu_baseline']}")
         result["cpu_oracle_threaded"] = cpu_oracle_threaded(w, d, torch)
         log(f"bench: oracle on a thread pool {result['cpu_oracle_threaded']}")
+        result["cpu_oracle_us_per_call"] = cpu_oracle_latency(DECODE_WORKLOADS)
+        log(f"bench: oracle per call on the small workloads {result['cpu_oracle_us_per_call']}")
     print(json.dumps(result), flush=True)
     return 0
 
