@@ -275,15 +275,22 @@ def test_unit_gain_bitwise(arn):
 
 
 def test_repeat_calls_bitwise_deterministic(arn, synth):
+    """100 repeated calls of the fused op and of the sum give the same bits."""
     w = synth.WORKLOADS["unit_offset_p8_128x8192"]
     d = synth.make_inputs(w, device=DEV)
     first = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
                       residual=d["residual"], in_place=False)
-    for _ in range(5):
+    s0 = torch.empty_like(d["inputs"][0])
+    arn.arn_sum_bf16(d["inputs"], s0)
+    s1 = torch.empty_like(s0)
+    for _ in range(100):
         again = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
                           residual=d["residual"], in_place=False)
         assert torch.equal(first[0].view(torch.uint8), again[0].view(torch.uint8))
         assert torch.equal(first[1], again[1]) and torch.equal(first[2], again[2])
+        s1.zero_()
+        arn.arn_sum_bf16(d["inputs"], s1)
+        assert torch.equal(s0.view(torch.int16), s1.view(torch.int16))
 
 
 def test_graph_replay_matches_eager(arn, synth):
