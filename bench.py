@@ -84,12 +84,12 @@ def out_sets_for(w) -> int:
     return max(1, min(MAX_OUT_SETS, -(-CACHE_FLUSH_BYTES // max(1, per))))
 
 
-def alloc_workload(w, torch, dev, out_sets: int = 1):
+def alloc_workload(w, torch, dev, out_sets: int = 1, seed=None):
     """Inputs of workload `w` on `dev`, and `out_sets` sets of output buffers
     (d["outs"]; d["out"], d["scales"], d["res_out"], d["sum_out"] are set 0)."""
     from all_reduce_rmsnorm_amd import synth
 
-    d = synth.make_inputs(w, device=dev)
+    d = synth.make_inputs(w, device=dev, seed=seed)
     rows, cols = w.rows, w.cols
     d["outs"] = []
     for _ in range(out_sets):
@@ -466,6 +466,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=None,
+                    help="input seed (default: the workload's own, 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true")
     ap.add_argument("--pmc-calib", action="store_true",
@@ -513,7 +515,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     log(f"bench: workload {w.name}, steps {args.steps}, warmup {args.warmup}")
     n_out = out_sets_for(w)
-    d = alloc_workload(w, torch, dev, out_sets=n_out)
+    d = alloc_workload(w, torch, dev, out_sets=n_out, seed=args.seed)
     torch.cuda.synchronize()
     fn = step_fn(w, d, arn)
     ms_per_step, kern_ms = time_steps(torch, fn, args.steps, args.warmup)
@@ -541,7 +543,8 @@ def main():
         "io_dtypes": "bf16 in, bf16 residual out, e4m3fn + f32 scales out" if not w.sum_only else "bf16 in, bf16 out",
         "data": "synthetic (seeded; inputs resident in HBM)",
         "output_sets": n_out,
-        "config": {"workload": w.name, "P": w.P, "rows": w.rows, "cols": w.cols,
+        "config": {"workload": w.name, "seed": w.seed if args.seed is None else args.seed,
+                   "P": w.P, "rows": w.rows, "cols": w.cols,
                    "residual": w.residual_std is not None, "eps": w.eps,
                    "weight_offset": w.weight_offset, "scale_ub": w.scale_ub,
                    "algorithmic_bytes_per_step": alg, "input_sha256": input_sha256(d, torch)},
