@@ -50,7 +50,8 @@ DECODE_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "tiny_p2_4x2
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
 # The device code, the host code that picks its launch shape and cache
 # policy, the ABI header whose constants both use, and the build flags: the
-# committed HBM-counter summary applies only while these are unchanged.
+# committed HBM-counter summary applies only while their code (comments
+# aside) is unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_kernels.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_tables.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8.hip"),
@@ -58,11 +59,23 @@ KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_k
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
 
 
+def _code_only(path: str) -> bytes:
+    """The file with comments and blank space removed, so that an edit of a
+    comment does not retire the counters taken on the code."""
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    if path.endswith(".py"):
+        text = re.sub(r"(?m)^\s*#.*$", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split()).encode()
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        h.update(_code_only(p))
     return h.hexdigest()[:16]
 
 

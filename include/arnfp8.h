@@ -42,7 +42,9 @@
  *     (the automatic launch shape depends only on rows, cols, P and the
  *     device), including calls replayed from a captured graph.
  *   - Concurrent calls on different streams must not share output buffers.
- *   - Non-finite inputs are not supported (the results are unspecified).
+ *   - Non-finite inputs are not supported (the results are unspecified), nor
+ *     are rows whose sum of squares leaves the fp32 range (|h| of order 1e18
+ *     and above): the row statistics are fp32.
  */
 #ifndef ARNFP8_H
 #define ARNFP8_H

@@ -142,3 +142,22 @@ def test_input_hash_is_reproducible_and_covers_every_tensor():
     c = dict(a)
     c["inputs"] = [a["inputs"][1], a["inputs"][0]] + a["inputs"][2:]
     assert bench.input_sha256(c, torch) != bench.input_sha256(a, torch)
+
+
+def test_counter_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    import bench
+
+    cpp = tmp_path / "k.hpp"
+    py = tmp_path / "b.py"
+    cpp.write_text("// a comment\nint f() { return 1; } /* block\ncomment */\n")
+    py.write_text("# a comment\nFLAGS = ['-O3']\n")
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(cpp), str(py)])
+    h0 = bench.kernel_source_hash()
+    cpp.write_text("// another comment\nint f() {   return 1; }\n")
+    py.write_text("# reworded\n\nFLAGS = ['-O3']\n")
+    assert bench.kernel_source_hash() == h0
+    cpp.write_text("int f() { return 2; }\n")
+    assert bench.kernel_source_hash() != h0
+    cpp.write_text("int f() { return 1; }\n")
+    py.write_text("FLAGS = ['-O2']\n")
+    assert bench.kernel_source_hash() != h0
