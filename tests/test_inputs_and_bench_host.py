@@ -161,3 +161,26 @@ def test_counter_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     cpp.write_text("int f() { return 1; }\n")
     py.write_text("FLAGS = ['-O2']\n")
     assert bench.kernel_source_hash() != h0
+
+
+def test_output_sets_exceed_twice_the_infinity_cache_on_the_headline():
+    """The timed prefill step writes a fresh output set on every call: the sets
+    together exceed 512 MiB, so no call finds its outputs in the 256 MB cache."""
+    import bench
+    from all_reduce_rmsnorm_amd import synth
+
+    w = synth.WORKLOADS[bench.DEFAULT_WORKLOAD]
+    n = bench.out_sets_for(w)
+    per_set = w.numel * (1 + 2) + 4 * w.rows  # fp8 + bf16 residual out + scales
+    assert n >= 2 and n * per_set >= bench.CACHE_FLUSH_BYTES
+    assert 1 <= bench.out_sets_for(synth.WORKLOADS["tiny_p2_4x256"]) <= bench.MAX_OUT_SETS
+
+
+def test_rotating_calls_each_function_in_turn():
+    import bench
+
+    seen = []
+    f = bench.rotating([lambda: seen.append(0), lambda: seen.append(1), lambda: seen.append(2)])
+    for _ in range(7):
+        f()
+    assert seen == [0, 1, 2, 0, 1, 2, 0]
