@@ -225,8 +225,6 @@ def graph_us_per_call(torch, fn, calls=100, reps=5):
 def cpu_baseline(w, d, torch, min_seconds=10.0, max_passes=3):
     """The oracle over every row of the workload (same bytes as the GPU),
     repeated until at least `min_seconds` of CPU work (at most `max_passes`)."""
-    import numpy as np
-
     import oracle
     from all_reduce_rmsnorm_amd import synth
 

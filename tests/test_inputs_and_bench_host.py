@@ -1,10 +1,8 @@
 """CPU checks of the input recipe and of bench.py's host logic (no GPU)."""
-import json
 import os
 import sys
 
 import numpy as np
-import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
