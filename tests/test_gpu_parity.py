@@ -403,7 +403,7 @@ def test_bad_launch_options_rejected(arn):
         assert e.value.status == 7, bad
 
 
-@pytest.mark.parametrize("ngpus", [1, 3, 8])
+@pytest.mark.parametrize("ngpus", [1, 3, 8, 64])
 def test_two_stage_share_and_staging_layout(arn, orc, ngpus):
     """Every rank's share: the staging slot holds the oracle's fp8 rows and
     scales of that share; the share's residual rows are updated, no other row
