@@ -561,3 +561,37 @@ def test_concurrent_calls_on_two_streams(arn, synth):
     for k in range(2):
         for got, want in zip(sets[k][1:], ref[k]):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), k
+
+
+@pytest.mark.parametrize("rank", [0, 5, 7])
+def test_two_stage_share_on_the_full_prefill_workload(arn, orc, synth, rank):
+    """One rank's share of the full prefill workload (8 ranks, 1024 rows each),
+    as the benchmark times it: seeded sampled rows of the staging slot and of
+    the residual against the oracle."""
+    import oracle as orc_mod
+
+    w = synth.WORKLOADS["prefill_p8_8192x7168"]
+    ngpus = 8
+    print(f"[share] full prefill, rank {rank} of {ngpus}", flush=True)
+    d = synth.make_inputs(w, device=DEV)
+    nbytes = arn.arnfp8_stage_bytes(w.rows, w.cols, ngpus)
+    staging = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+    res_out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=DEV)
+    arn.arnfp8_run_share(d["inputs"], d["residual"], res_out, staging, d["gamma"], w.eps,
+                         w.weight_offset, w.scale_ub, ngpus=ngpus, rank=rank)
+    torch.cuda.synchronize()
+    first, count = orc_mod.share_rows(w.rows, ngpus, rank)
+    S = -(-w.rows // ngpus)
+    local = np.unique(np.concatenate([[0, count - 1],
+                                      np.random.default_rng(rank).choice(count, 62, replace=False)]))
+    idx = torch.from_numpy(first + local).to(DEV)
+    xs_h = [x.index_select(0, idx).cpu() for x in d["inputs"]]
+    q, s, h = orc.arnfp8([_bits(x) for x in xs_h], _bits(d["gamma"].cpu()), w.eps,
+                         w.weight_offset, w.scale_ub,
+                         residual_in=_bits(d["residual"].index_select(0, idx).cpu()))
+    got = staging.cpu().numpy()
+    data = got[: S * w.cols].reshape(S, w.cols)
+    scales = got[S * w.cols: S * w.cols + 4 * S].view(np.float32)
+    assert_fp8_close(data[local], q)
+    assert_scales_close(scales[local], s)
+    assert_bits_equal(_bits(res_out.index_select(0, idx)), h, "share residual")
