@@ -354,10 +354,13 @@ def test_errors_raise_before_launch(arn):
     torch.cuda.synchronize()
 
 
-def test_unfused_two_launch_chain_is_bitwise_equal(arn, synth):
+@pytest.mark.parametrize("name", ["unit_offset_p8_128x8192", "prefill_p8_8192x7168"])
+def test_unfused_two_launch_chain_is_bitwise_equal(arn, synth, name):
     """arn_sum_bf16 to HBM, then the fused kernel with P = 1 on the sum: the
-    same bytes as the single fused launch (the fusion changes no result)."""
-    w = synth.WORKLOADS["unit_offset_p8_128x8192"]
+    same bytes as the single fused launch (the fusion changes no result), on
+    the benchmark's prefill workload too."""
+    w = synth.WORKLOADS[name]
+    print(f"[fused] unfused chain {name}", flush=True)
     d = synth.make_inputs(w, device=DEV)
     fused = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
                       residual=d["residual"], in_place=False)
