@@ -324,8 +324,10 @@ def test_graph_replay_matches_eager(arn, synth):
         _ = (d["inputs"][0].float() * 2.0).sum().item()  # unrelated eager work between replays
 
 
-def test_in_place_residual_matches_out_of_place(arn, synth):
-    w = synth.WORKLOADS["decode_p4_32x7168"]
+@pytest.mark.parametrize("name", ["decode_p4_32x7168", "prefill_p8_8192x7168"])
+def test_in_place_residual_matches_out_of_place(arn, synth, name):
+    w = synth.WORKLOADS[name]
+    print(f"[fused] in place vs out of place {name}", flush=True)
     d = synth.make_inputs(w, device=DEV)
     res_copy = d["residual"].clone()
     a = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset, w.scale_ub,
