@@ -18,7 +18,7 @@ from tests._util import (assert_bits_equal, assert_e5m2_close, assert_fp8_close,
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-N_CASES = 48
+N_CASES = 160
 MAX_ELEMS = 400_000
 
 
