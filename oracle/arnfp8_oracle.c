@@ -32,7 +32,10 @@
  * P = 1); gamma + weight_offset is one fp32 add (not re-rounded to bf16); eps
  * is added to the mean square inside the square root; amax is taken over the
  * post-gain normalised row; the fp8 code is decided from an fp32 value
- * (fl32(y / scale)), round-to-nearest-even with saturation at +-448.
+ * (fl32(y / scale)), round-to-nearest-even with saturation at +-448; with
+ * eps = 0 an all-zero row normalises to y = 0 (floor scale, zero codes); eps
+ * must be finite and >= 0, weight_offset finite and scale_ub > 0 (calls with
+ * other values return ORACLE_BAD_ARG).
  *
  * The norm statistics and the normalised row are computed in fp64, so the
  * oracle's y is the exact value up to a few fp64 roundings.
@@ -186,6 +189,20 @@ static int check_common(const uint16_t *const *inputs, int P, int64_t rows,
     return ORACLE_OK;
 }
 
+/* The norm's scalars: epsilon is a stabilising term added to the mean square,
+ * so it must be finite and not negative; the weight offset is added to gamma,
+ * so it must be finite; scale_ub bounds the scale from above, so it must be
+ * positive (+inf: no bound).  `check_ub` is 0 for the MX output, which has no
+ * scale_ub. */
+static int check_scalars(float eps, float weight_offset, float scale_ub, int check_ub)
+{
+    if (!isfinite(eps) || eps < 0.0f || !isfinite(weight_offset))
+        return ORACLE_BAD_ARG;
+    if (check_ub && !(scale_ub > 0.0f))
+        return ORACLE_BAD_ARG;
+    return ORACLE_OK;
+}
+
 /* One element of the rank-order sum: start from rank 0's value, add ranks
  * 1..P-1 in order, each add one fp32 rounding; round the total to bf16 once. */
 static uint16_t rank_order_sum(const uint16_t *const *inputs, int P, int64_t k)
@@ -226,12 +243,17 @@ static void norm_row(const uint16_t *const *inputs, int P, const uint16_t *resid
         h[j] = (double)oracle_bf16_to_f32(hb);
     }
 
-    /* RMSNorm: r = 1 / sqrt(mean(h^2) + eps), y = h * r * g. */
+    /* RMSNorm: r = 1 / sqrt(mean(h^2) + eps), y = h * r * g.  With eps = 0
+     * an all-zero row has mean(h^2) + eps = 0 and nothing to normalise: the
+     * reading taken is y = 0 (so the row gets the floor scale and zero codes,
+     * never a NaN).  In fp64 the sum of squares of bf16 values is zero only
+     * when every h is zero, so no other row takes this branch. */
     double sumsq = 0.0;
     for (int64_t j = 0; j < cols; ++j)
         sumsq += h[j] * h[j];
     double ms = sumsq / (double)cols;
-    double r = 1.0 / sqrt(ms + (double)eps);
+    double den = ms + (double)eps;
+    double r = den > 0.0 ? 1.0 / sqrt(den) : 0.0;
 
     for (int64_t j = 0; j < cols; ++j) {
         float g = oracle_bf16_to_f32(gamma[j]) + weight_offset; /* fp32 add */
@@ -256,6 +278,9 @@ static int fused_per_row(const uint16_t *const *inputs, int P, const uint16_t *r
     if (st != ORACLE_OK)
         return st;
     if (out_fp8 == NULL || scales == NULL || gamma == NULL)
+        return ORACLE_BAD_ARG;
+
+    if (check_scalars(eps, weight_offset, scale_ub, 1) != ORACLE_OK)
         return ORACLE_BAD_ARG;
 
     const float fmax = e5m2 ? 57344.0f : 448.0f;
@@ -321,7 +346,7 @@ int oracle_norm_rows(const uint16_t *const *inputs, int P, const uint16_t *resid
     int st = check_common(inputs, P, rows, cols);
     if (st != ORACLE_OK)
         return st;
-    if (gamma == NULL || y == NULL)
+    if (gamma == NULL || y == NULL || check_scalars(eps, weight_offset, 0.0f, 0) != ORACLE_OK)
         return ORACLE_BAD_ARG;
     double *h = (double *)malloc((size_t)cols * sizeof(double));
     if (h == NULL)
@@ -383,7 +408,8 @@ int oracle_arnfp8_mx(const uint16_t *const *inputs, int P,
     int st = check_common(inputs, P, rows, cols);
     if (st != ORACLE_OK)
         return st;
-    if (out_fp8 == NULL || block_scales == NULL || gamma == NULL || cols % 32 != 0)
+    if (out_fp8 == NULL || block_scales == NULL || gamma == NULL || cols % 32 != 0 ||
+        check_scalars(eps, weight_offset, 0.0f, 0) != ORACLE_OK)
         return ORACLE_BAD_ARG;
     double *h = (double *)malloc((size_t)cols * sizeof(double));
     double *y = (double *)malloc((size_t)cols * sizeof(double));

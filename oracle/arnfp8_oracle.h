@@ -62,12 +62,15 @@ int oracle_sum_bf16(const uint16_t *const *inputs, int P, uint16_t *out,
  *   h   = bf16_rne(fp32(s) + fp32(residual_in)) if residual_in, else s
  *   residual_out <- h (if residual_out; may equal residual_in)
  *   g_j = fl32(fp32(gamma_j) + weight_offset)
- *   r   = 1 / sqrt(mean_j(h_j^2) + eps)                          (fp64)
+ *   r   = 1 / sqrt(mean_j(h_j^2) + eps), or 0 when mean + eps == 0 (an
+ *         all-zero row with eps = 0: y = 0, floor scale, zero codes)  (fp64)
  *   y_j = h_j * r * g_j                                           (fp64)
  *   amax = fl32(max_j |y_j|)
  *   scale = max(min(amax, scale_ub) / 448, 1 / (448 * 512))        (fp32)
  *   q_j = e4m3fn_rne_sat(fl32(y_j / scale))
- * scales[i] = scale.  out_fp8 holds the q codes. */
+ * scales[i] = scale.  out_fp8 holds the q codes.
+ * eps must be finite and >= 0, weight_offset finite, scale_ub > 0 (+inf: no
+ * bound); otherwise ORACLE_BAD_ARG (the MX variant checks eps and the offset). */
 int oracle_arnfp8(const uint16_t *const *inputs, int P,
                   const uint16_t *residual_in, uint16_t *residual_out,
                   uint8_t *out_fp8, float *scales, const uint16_t *gamma,

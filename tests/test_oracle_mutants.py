@@ -24,7 +24,7 @@ MUTANTS = {
     "reverse_rank_order": ("float acc = oracle_bf16_to_f32(inputs[0][k]);\n    for (int p = 1; p < P; ++p)\n        acc = acc + oracle_bf16_to_f32(inputs[p][k]);",
                            "float acc = oracle_bf16_to_f32(inputs[P - 1][k]);\n    for (int p = P - 2; p >= 0; --p)\n        acc = acc + oracle_bf16_to_f32(inputs[p][k]);"),
     "residual_not_rounded_once": ("hb = oracle_f32_to_bf16(t);", "hb = oracle_f32_to_bf16(t + 1e-3f * t);"),
-    "drop_eps": ("sqrt(ms + (double)eps)", "sqrt(ms)"),
+    "drop_eps": ("double den = ms + (double)eps;", "double den = ms;"),
     "sum_not_mean": ("double ms = sumsq / (double)cols;", "double ms = sumsq;"),
     "gamma_reversed": ("oracle_bf16_to_f32(gamma[j])", "oracle_bf16_to_f32(gamma[cols - 1 - j])"),
     "drop_weight_offset": ("oracle_bf16_to_f32(gamma[j]) + weight_offset;", "oracle_bf16_to_f32(gamma[j]);"),
@@ -42,7 +42,11 @@ MUTANTS = {
                               "for (int i = 0; i < n / 2; ++i)\n        if (fabs(v[i]) > amax)"),
     "share_floor_not_ceil": ("int64_t S = (rows + ngpus - 1) / ngpus;\n    int64_t lo", "int64_t S = rows / ngpus + 1;\n    int64_t lo"),
     "stage_no_padding": ("(scale_bytes + simd_width - 1) / simd_width * simd_width", "scale_bytes"),
-    "rsqrt_not_inverse": ("double r = 1.0 / sqrt(ms + (double)eps);", "double r = 1.0 / (ms + (double)eps);"),
+    "rsqrt_not_inverse": ("1.0 / sqrt(den)", "1.0 / den"),
+    "eps_zero_row_nan": ("double r = den > 0.0 ? 1.0 / sqrt(den) : 0.0;", "double r = 1.0 / sqrt(den);"),
+    "accept_negative_eps": ("!isfinite(eps) || eps < 0.0f ||", "!isfinite(eps) ||"),
+    "accept_nonfinite_eps": ("!isfinite(eps) || eps < 0.0f ||", "eps < 0.0f ||"),
+    "accept_nonpositive_ub": ("if (check_ub && !(scale_ub > 0.0f))", "if (check_ub && scale_ub < 0.0f)"),
 }
 
 

@@ -279,3 +279,60 @@ def test_library_fp8_conversion_agrees_on_decision_values(orc):
         ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
         mism += int(np.sum(ref != q[i]))
     assert mism == 0
+
+
+# ------------------------------------------------ eps = 0 and bad scalars --
+
+@pytest.mark.parametrize("with_res", [False, True])
+def test_eps_zero_all_zero_row_takes_floor_and_zero_codes(orc, with_res):
+    # The Mojo docs put no lower bound on epsilon.  With eps = 0 an all-zero
+    # row has mean(h^2) + eps = 0: the reading is y = 0, so the scale is the
+    # floor and every code is a zero (never the NaN code 0x7F / 0xFF).
+    # Row 1 mixes -0 and +0 (h keeps its sign, so codes may be +0 or -0);
+    # row 2 is an ordinary row next to them, which must be unaffected.
+    cols = 64
+    x = np.zeros((3, cols), dtype=np.uint16)
+    x[1, ::2] = 0x8000  # -0.0
+    x[2] = bf_arr([[1.0, -2.0] * (cols // 2)])[0]
+    res = np.zeros((3, cols), dtype=np.uint16) if with_res else None
+    q, s, h = orc.arnfp8([x], ones_gamma(cols), 0.0, 0.0, 1200.0, residual_in=res)
+    assert np.all(s[:2] == np.float32(SCALE_FLOOR))
+    assert not np.any((q & 0x7F) == 0x7F)
+    assert np.all((q[:2] & 0x7F) == 0)
+    # row 2: ms = 2.5, y = (1, -2) / sqrt(2.5): codes 224 and -448 exactly
+    vals = e4m3_val(q[2])
+    assert np.all(vals[0::2] == 224.0) and np.all(vals[1::2] == -448.0)
+    assert s[2] == np.float32(f32(f32(2.0 / math.sqrt(2.5)) / 448.0))
+
+
+def test_eps_zero_tiny_row_still_normalises(orc):
+    # Only mean + eps == 0 takes the zero branch: a row of tiny (subnormal
+    # bf16) values with eps = 0 still normalises to unit RMS.
+    cols = 32
+    k = 2.0 ** -130  # a bf16 subnormal; k^2 is exact in fp64
+    x = bf_arr([[k] * cols])
+    q, s, _ = orc.arnfp8([x], ones_gamma(cols), 0.0, 0.0, 1200.0)
+    assert s[0] == np.float32(f32(1.0 / 448.0))
+    assert np.all(e4m3_val(q) == 448.0)
+
+
+@pytest.mark.parametrize("eps,woff,ub", [(-1e-6, 0.0, 1.0), (float("nan"), 0.0, 1.0),
+                                         (float("inf"), 0.0, 1.0), (1e-6, float("nan"), 1.0),
+                                         (1e-6, float("inf"), 1.0), (1e-6, 0.0, 0.0),
+                                         (1e-6, 0.0, -2.0), (1e-6, 0.0, float("nan"))])
+def test_bad_scalars_are_rejected(orc, eps, woff, ub):
+    x = bf_arr([[1.0] * 16])
+    with pytest.raises(ValueError):
+        orc.arnfp8([x], ones_gamma(16), eps, woff, ub)
+    with pytest.raises(ValueError):
+        orc.arnfp8_e5m2([x], ones_gamma(16), eps, woff, ub)
+
+
+def test_infinite_scale_ub_means_no_bound(orc):
+    rng = np.random.default_rng(31)
+    xs = [rand_bf16(rng, (6, 128), 4.0)]
+    gamma = rand_bf16(rng, (128,), 0.2, 1.0)
+    a = orc.arnfp8(xs, gamma, 1e-6, 0.0, float("inf"))
+    b = orc.arnfp8(xs, gamma, 1e-6, 0.0, 1e30)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)

@@ -169,3 +169,30 @@ def test_norm_rows_closed_form(orc):
     y = orc.norm_rows([bf_arr([row])], gamma, 0.0, 0.0)
     assert y[0, 5] == pytest.approx(-math.sqrt(cols) * 1.5, rel=1e-15)
     assert np.all(np.delete(y[0], 5) == 0.0)
+
+
+def test_eps_zero_all_zero_rows_e5m2_and_mx(orc):
+    # eps = 0 on an all-zero row gives y = 0: e5m2 takes the floor scale and
+    # zero codes, MX takes the smallest E8M0 scale (-127) and zero codes; an
+    # ordinary row beside them is unaffected.
+    cols = 64
+    x = np.zeros((2, cols), dtype=np.uint16)
+    x[1] = bf_arr([1.0, -2.0] * (cols // 2))
+    gamma = bf_arr([1.0] * cols)
+    q, s, _ = orc.arnfp8_e5m2([x], gamma, 0.0, 0.0, 1200.0)
+    assert s[0] == np.float32(f32(1.0 / (E5M2_MAX * 512.0)))
+    assert np.all((q[0] & 0x7F) == 0)
+    assert not np.any((q & 0x7C) == 0x7C)
+    assert np.all(e5m2_val(q[1])[1::2] == -E5M2_MAX)
+    qm, bs, _ = orc.arnfp8_mx([x], gamma, 0.0, 0.0)
+    assert np.all(bs[0] == 0) and np.all((qm[0] & 0x7F) == 0)
+    # row 1: max |y| = 2 / sqrt(2.5) = 1.26..., floor(log2) = 0, e = -8
+    assert np.all(bs[1] == 127 - 8)
+    assert not np.any((qm & 0x7F) == 0x7F)
+
+
+@pytest.mark.parametrize("eps,woff", [(-1.0, 0.0), (float("nan"), 0.0), (1e-6, float("inf"))])
+def test_mx_bad_scalars_are_rejected(orc, eps, woff):
+    x = bf_arr([[1.0] * 32])
+    with pytest.raises(ValueError):
+        orc.arnfp8_mx([x], bf_arr([1.0] * 32), eps, woff)
