@@ -32,7 +32,7 @@ MAX_COLS = 65536
 STATUS = {
     0: "ARNFP8_OK", 1: "ARNFP8_NULL_POINTER", 2: "ARNFP8_MISALIGNED", 3: "ARNFP8_BAD_SHAPE",
     4: "ARNFP8_BAD_P", 5: "ARNFP8_ALIAS", 6: "ARNFP8_HIP_ERROR", 7: "ARNFP8_BAD_CONFIG",
-    8: "ARNFP8_BAD_SHARE", 9: "ARNFP8_BAD_FORMAT",
+    8: "ARNFP8_BAD_SHARE", 9: "ARNFP8_BAD_FORMAT", 10: "ARNFP8_BAD_SCALAR",
 }
 FMT_E4M3FN = 0
 FMT_E5M2 = 1

@@ -14,6 +14,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <cfloat>
 
 #include "arnfp8.h"
 #include "arnfp8_kernels.hpp"
@@ -37,6 +38,16 @@ int check_shape(int64_t rows, int64_t cols, int P) {
   if (P < 1 || P > ARNFP8_MAX_P) return ARNFP8_BAD_P;
   if (rows < 0 || cols <= 0 || cols % 8 != 0 || cols > ARNFP8_MAX_COLS) return ARNFP8_BAD_SHAPE;
   if (rows > INT64_MAX / (2 * cols)) return ARNFP8_BAD_SHAPE;
+  return ARNFP8_OK;
+}
+
+// The norm's scalars: eps finite and >= 0, weight_offset finite, and (for the
+// per-row formats) scale_ub > 0, +inf meaning no bound.  NaN fails every
+// comparison below, so it is rejected too.
+int check_scalars(float eps, float weight_offset, float scale_ub, bool check_ub) {
+  if (!(eps >= 0.0f && eps <= FLT_MAX) || !(weight_offset >= -FLT_MAX && weight_offset <= FLT_MAX))
+    return ARNFP8_BAD_SCALAR;
+  if (check_ub && !(scale_ub > 0.0f)) return ARNFP8_BAD_SCALAR;
   return ARNFP8_OK;
 }
 
@@ -275,6 +286,8 @@ extern "C" int arnfp8_run_fmt(const void *const *inputs, const void *residual_in
       out_format != ARNFP8_FMT_MXFP8)
     return ARNFP8_BAD_FORMAT;
   if (out_format == ARNFP8_FMT_MXFP8 && cols % 32 != 0) return ARNFP8_BAD_SHAPE;
+  st = check_scalars(eps, weight_offset, scale_ub, out_format != ARNFP8_FMT_MXFP8);
+  if (st != ARNFP8_OK) return st;
   if (rows == 0) return ARNFP8_OK;
   RowArgs a;
   st = prepare_fused(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
@@ -319,6 +332,8 @@ extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_
   int st = check_shape(rows, cols, P);
   if (st != ARNFP8_OK) return st;
   if (ngpus < 1 || rank < 0 || rank >= ngpus) return ARNFP8_BAD_SHARE;
+  st = check_scalars(eps, weight_offset, scale_ub, true);
+  if (st != ARNFP8_OK) return st;
   if (rows == 0) return ARNFP8_OK;
   st = check_inputs(inputs, P);
   if (st != ARNFP8_OK) return st;
@@ -405,6 +420,8 @@ extern "C" const char *arnfp8_status_string(int status) {
     case ARNFP8_BAD_CONFIG: return "invalid launch configuration";
     case ARNFP8_BAD_SHARE: return "bad share: ngpus must be >= 1 and 0 <= rank < ngpus";
     case ARNFP8_BAD_FORMAT: return "unknown output format";
+    case ARNFP8_BAD_SCALAR:
+      return "bad scalar: eps must be finite and >= 0, weight_offset finite, scale_ub > 0";
     default: return "unknown status";
   }
 }

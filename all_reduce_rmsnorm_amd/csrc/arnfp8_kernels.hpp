@@ -455,7 +455,10 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
     // measured: decode 3.49 against 3.61 us per call with the IEEE square root
     // and divisions).  The division by the format maximum stays IEEE, so a
     // clamped scale is exactly fl32(scale_ub / fmax).
-    const float r = __builtin_amdgcn_rsqf(tot * a.inv_cols + a.eps);
+    // eps = 0 on an all-zero row leaves nothing to normalise: r = 0 makes the
+    // row all zeros (floor scale, zero codes) instead of 0 * inf = NaN.
+    const float den = tot * a.inv_cols + a.eps;
+    const float r = den > 0.0f ? __builtin_amdgcn_rsqf(den) : 0.0f;
     float cq = 0.0f;
     if constexpr (FMT != kFmtMx) {
       const float amax = m * r;

@@ -59,19 +59,57 @@ extern "C" {
 #define ARNFP8_MAX_P 8
 #define ARNFP8_MAX_COLS 65536
 
-/* Status codes. */
+/*
+ * Status codes.  Every entry point returns one; all of them except
+ * ARNFP8_HIP_ERROR are decided on the host before anything is launched.
+ * Returning a status code from a first phase that validates the arguments is
+ * the convention of Huawei CANN aclnnAlltoAllQuantMatmul (Returns: a status
+ * code; the first-phase API validates the input parameters).  The checks
+ * themselves are the ones b12x PR #283 "PCIeTwoShotBF16" is asked to make in
+ * review: payload and caller-provided output tensors checked for alignment,
+ * shape and capacity before any device launch, so that no launch reads
+ * misaligned data or writes out of bounds.
+ */
 #define ARNFP8_OK 0
-#define ARNFP8_NULL_POINTER 1 /* a required pointer is NULL                      */
-#define ARNFP8_MISALIGNED 2   /* a pointer breaks the alignment rule above       */
-#define ARNFP8_BAD_SHAPE 3    /* rows < 0, cols <= 0, cols % 8, cols too large,
-                                 or the byte size overflows int64              */
-#define ARNFP8_BAD_P 4        /* P outside [1, ARNFP8_MAX_P]                     */
-#define ARNFP8_ALIAS 5        /* an output overlaps an input or another output
-                                 (residual_out == residual_in is allowed)      */
-#define ARNFP8_HIP_ERROR 6    /* the kernel launch call itself failed            */
-#define ARNFP8_BAD_CONFIG 7   /* an arnfp8_run_ex launch option is invalid       */
-#define ARNFP8_BAD_SHARE 8    /* ngpus < 1, or rank outside [0, ngpus)           */
-#define ARNFP8_BAD_FORMAT 9   /* unknown out_format                              */
+/* A required pointer is NULL.  CANN aclnnAlltoAllQuantMatmul (constraints:
+ * the inputs and the output are not null pointers). */
+#define ARNFP8_NULL_POINTER 1
+/* A pointer breaks the alignment rule above.  b12x PR #283 review (the payload
+ * must be 16-byte aligned, as the kernel's vector loads assume; misaligned
+ * tensors are rejected before launch). */
+#define ARNFP8_MISALIGNED 2
+/* rows < 0, cols <= 0, cols % 8, cols > ARNFP8_MAX_COLS, or the byte size
+ * overflows int64.  b12x PR #283 (Behavior: accepts() rejects a tensor whose
+ * size does not fit the row width or exceeds the row capacity; Validation:
+ * rejections by dtype, row width, row count and capacity are tested); CANN
+ * aclnnAlltoAllQuantMatmul (constraints: upper and lower bounds on the
+ * sizes). */
+#define ARNFP8_BAD_SHAPE 3
+/* P outside [1, ARNFP8_MAX_P].  Mojo docs "allreduce_rmsnorm_fp8" (rank_sigs:
+ * 8 signal slots, so at most 8 ranks); b12x PR #283 (world sizes 2, 4, 8). */
+#define ARNFP8_BAD_P 4
+/* An output overlaps an input or another output (residual_out == residual_in
+ * is allowed).  b12x PR #283 review (caller-provided output tensors are
+ * validated before their pointers reach device code, to prevent incorrect
+ * writes). */
+#define ARNFP8_ALIAS 5
+/* The kernel launch call itself failed (the HIP runtime's error). */
+#define ARNFP8_HIP_ERROR 6
+/* An arnfp8_run_ex launch option is invalid (this library's own tuning
+ * interface; no page defines it). */
+#define ARNFP8_BAD_CONFIG 7
+/* ngpus < 1, or rank outside [0, ngpus).  Mojo docs "allreduce_rmsnorm_fp8"
+ * (the 2-stage path: ngpus ranks, each owning ceildiv(rows, ngpus) rows). */
+#define ARNFP8_BAD_SHARE 8
+/* Unknown out_format.  CANN aclnnAlltoAllQuantMatmul (x1QuantDtype and the
+ * quantisation modes name the supported output types). */
+#define ARNFP8_BAD_FORMAT 9
+/* eps NaN, infinite or negative; weight_offset NaN or infinite; or, for the
+ * per-row formats, scale_ub NaN or <= 0 (+inf is allowed: no upper bound).
+ * Mojo docs "allreduce_rmsnorm_fp8" (Args: epsilon is the RMSNorm's
+ * stabilising term, weight_offset an additive offset of gamma, scale_ub the
+ * upper bound of the scale clamp). */
+#define ARNFP8_BAD_SCALAR 10
 
 /*
  * arnfp8_run -- the fused epilogue.  For every row i and column j:
@@ -80,7 +118,7 @@ extern "C" {
  *   h    = bf16_rne(fp32(s) + fp32(residual_in[i,j]))  if residual_in, else s
  *   residual_out[i,j] = h                               if residual_out
  *   g_j  = fp32(gamma[j]) + weight_offset                          (fp32)
- *   r    = 1 / sqrt(sum_j h_j^2 / cols + eps)
+ *   r    = 1 / sqrt(sum_j h_j^2 / cols + eps)   (0 if that sum is 0: see eps)
  *   amax = max_j |h_j * g_j| * r
  *   scale = max(min(amax, scale_ub) / 448, 1 / (448 * 512))
  *   out_fp8[i,j] = e4m3fn(clamp(h_j * g_j * r / scale, -448, 448)),
@@ -93,7 +131,16 @@ extern "C" {
  * out_fp8      device e4m3fn [rows, cols] (OCP FP8 E4M3: bias 7, max 448)
  * scales       device fp32 [rows] (the [rows, 1] per-row scales)
  * gamma        device bf16 [cols]
- * eps, weight_offset, scale_ub   fp32 scalars, used as given
+ * eps          fp32, finite and >= 0.  With eps = 0 a row whose mean square is
+ *              0 (all h zero) has nothing to normalise: r is taken as 0, so
+ *              the row gets the floor scale and zero codes (never a NaN code).
+ *              The mean square is fp32 here, so with eps = 0 a row whose
+ *              mean square is not a normal fp32 number (RMS below about
+ *              1e-19) lies outside the supported range, like rows whose
+ *              sum of squares overflows.
+ * weight_offset fp32, finite.
+ * scale_ub     fp32, > 0 (+inf: no upper bound).
+ *              Any other eps, weight_offset or scale_ub: ARNFP8_BAD_SCALAR.
  * Norm and scale arithmetic is fp32.  r comes from the hardware reciprocal
  * square root of fl32(sum_j h_j^2 * fl32(1 / cols)) + eps, and 1 / scale from
  * the hardware reciprocal (each within 1 ulp); the division by 448 is IEEE, so
@@ -158,7 +205,8 @@ int arnfp8_run_ex(const void *const *inputs, const void *residual_in, void *resi
  *   ARNFP8_FMT_E5M2    as arnfp8_run with the e5m2 maximum 57344 in place of
  *                      448: scale = max(min(amax, scale_ub) / 57344,
  *                      1 / (57344 * 512)); out_fp8 holds OCP e5m2 codes.
- *   ARNFP8_FMT_MXFP8   no per-row scale and no scale_ub (ignored): every block
+ *   ARNFP8_FMT_MXFP8   no per-row scale and no scale_ub (ignored, not
+ *                      validated): every block
  *                      of 32 consecutive values of a row gets the shared
  *                      exponent e = floor(log2(max |y|)) - 8, clamped to
  *                      [-127, 127] (-127 for an all-zero block), and its values
@@ -231,7 +279,9 @@ int arnfp8_run_share(const void *const *inputs, const void *residual_in, void *r
 #define ARNFP8_CVT_BF16 16
 int arnfp8_convert_f32(const float *in, void *out, int64_t n, int format, hipStream_t stream);
 
-/* Human-readable text for a status code (a static string; never NULL). */
+/* Human-readable text for a status code (a static string; never NULL; "unknown
+ * status" for a code not listed above).  The text of each code restates the
+ * rule whose source is cited at the code's definition. */
 const char *arnfp8_status_string(int status);
 
 #ifdef __cplusplus

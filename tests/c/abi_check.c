@@ -32,6 +32,8 @@ int main(void) {
   expect("misaligned out", arnfp8_run(inputs, NULL, NULL, (char *)out + 8, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, NULL), ARNFP8_MISALIGNED);
   expect("alias", arnfp8_run(inputs, NULL, (void *)inputs[1], out, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, NULL), ARNFP8_ALIAS);
   expect("rows 0", arnfp8_run(inputs, NULL, NULL, NULL, NULL, NULL, 1e-6f, 0.0f, 1.0f, 0, 256, 2, NULL), ARNFP8_OK);
+  expect("negative eps", arnfp8_run(inputs, NULL, NULL, out, scales, gamma, -1.0f, 0.0f, 1.0f, 4, 256, 2, NULL), ARNFP8_BAD_SCALAR);
+  expect("zero scale_ub", arnfp8_run(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 0.0f, 4, 256, 2, NULL), ARNFP8_BAD_SCALAR);
   opt.threads = 96;
   expect("bad threads", arnfp8_run_ex(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, NULL, &opt), ARNFP8_BAD_CONFIG);
   expect("bad format", arnfp8_run_fmt(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, 42, NULL, NULL), ARNFP8_BAD_FORMAT);

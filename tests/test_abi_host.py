@@ -16,6 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER_DIR = os.path.join(ROOT, "include")
 
 OK, NULLP, MISALIGNED, BAD_SHAPE, BAD_P, ALIAS = 0, 1, 2, 3, 4, 5
+BAD_SCALAR = 10
 
 
 @pytest.fixture(scope="module")
@@ -63,7 +64,7 @@ def test_library_is_built_for_gfx950():
 def test_status_strings(L):
     import all_reduce_rmsnorm_amd as arn
 
-    for code in range(0, 8):
+    for code in range(0, 11):
         s = arn.arnfp8_status_string(code)
         assert s and s != "unknown status"
     assert arn.arnfp8_status_string(99) == "unknown status"
@@ -273,3 +274,36 @@ def test_binding_refuses_buffers_smaller_than_the_shape():
                              1.0, ngpus=2, rank=0)
     with pytest.raises(ValueError, match="out holds"):
         arn.arnfp8_convert_f32(torch.zeros(16), torch.zeros(8, dtype=torch.uint8), arn.FMT_E4M3FN)
+
+
+NAN, INF = float("nan"), float("inf")
+
+
+@pytest.mark.parametrize("eps,woff,ub", [(-1e-6, 0.0, 1.0), (NAN, 0.0, 1.0), (INF, 0.0, 1.0),
+                                         (1e-6, NAN, 1.0), (1e-6, -INF, 1.0), (1e-6, 0.0, 0.0),
+                                         (1e-6, 0.0, -3.0), (1e-6, 0.0, NAN)])
+def test_bad_scalars_rejected_before_launch(L, eps, woff, ub):
+    """eps must be finite and >= 0, weight_offset finite, scale_ub > 0; the
+    check comes before the rows == 0 shortcut, so no call here launches."""
+    x0, x1 = BASE, BASE + 10 * MB
+    args = (_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 200 * MB, BASE + 300 * MB,
+            eps, woff, ub)
+    for rows in (0, 4):
+        assert L.arnfp8_run(*args, rows, 256, 2, None) == BAD_SCALAR
+        assert L.arnfp8_run_ex(*args, rows, 256, 2, None, None) == BAD_SCALAR
+        assert L.arnfp8_run_fmt(*args, rows, 256, 2, 1, None, None) == BAD_SCALAR
+        assert L.arnfp8_run_share(_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 300 * MB,
+                                  eps, woff, ub, rows, 256, 2, 4, 1, None) == BAD_SCALAR
+    # the MX output has no scale_ub: only eps and the offset are checked
+    only_ub_bad = eps == 1e-6 and woff == 0.0
+    mx = L.arnfp8_run_fmt(*args, 0, 256, 2, 2, None, None)
+    assert mx == (OK if only_ub_bad else BAD_SCALAR)
+
+
+def test_good_scalar_edges_are_accepted(L):
+    """eps = 0, scale_ub = +inf and large finite values pass validation (rows
+    = 0: nothing is launched)."""
+    x0, x1 = BASE, BASE + 10 * MB
+    for eps, woff, ub in ((0.0, 0.0, 1.0), (1e-6, 0.0, INF), (3e38, -3e38, 1e-30)):
+        assert L.arnfp8_run(_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 200 * MB,
+                            BASE + 300 * MB, eps, woff, ub, 0, 256, 2, None) == OK

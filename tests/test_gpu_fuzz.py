@@ -3,7 +3,8 @@
 Each case draws its own shape (ragged columns, 1 to a few hundred rows), P,
 residual mode (none, read only, written only, read and written, in place),
 output format, launch shape (lanes, chunks per lane, grid, store policy),
-value scale, zero rows, shared outliers, eps, weight offset and scale_ub, all
+value scale, zero rows, shared outliers, eps (0 included: zero rows then take
+the all-zero result), weight offset and scale_ub, all
 from one seed, so a failure names a case that can be rerun alone.  The bar is
 the parity bar of the other GPU tests; the share of exactly equal codes is
 only checked on cases large enough for it to mean something.
@@ -62,7 +63,8 @@ def _case(i):
     std = float(rng.choice([1e-3, 0.5, 30.0]))
     woff = float(rng.choice([0.0, 1.0]))
     return dict(fmt=fmt, rows=rows, cols=cols, P=P, res_mode=res_mode, std=std, woff=woff,
-                eps=float(rng.choice([1e-6, 1e-5, 1e-3])), ub=float(rng.choice([1.0, 64.0, 1200.0])),
+                eps=float(rng.choice([0.0, 1e-6, 1e-5, 1e-3])),
+                ub=float(rng.choice([1.0, 64.0, 1200.0])),
                 zero_rows=bool(rng.random() < 0.3), outliers=bool(rng.random() < 0.3),
                 launch=_launch(rng, cols // 8), grid=int(rng.integers(1, rows + 4)),
                 seed=int(rng.integers(0, 2**31)))

@@ -145,34 +145,6 @@ def test_fused_workload_full_size(arn, orc, synth, name):
                          h["residual"], out, scales, res_out)
 
 
-def test_fused_prefill_full_size_sampled_rows(arn, orc, synth):
-    """The prefill workload at its full size, generated on the GPU; the oracle
-    checks a seeded sample of rows, and size-free properties cover every row."""
-    w = synth.WORKLOADS["prefill_p8_8192x7168"]
-    print(f"[fused] workload {w.name} (sampled rows)", flush=True)
-    d = synth.make_inputs(w, device=DEV)
-    res0 = d["residual"].clone()
-    out, scales, res_out = run_fused(arn, d["inputs"], d["gamma"], w.eps, w.weight_offset,
-                                     w.scale_ub, residual=d["residual"], in_place=True)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, w.rows - 1], rng.choice(w.rows, 253, replace=False)]))
-    idx = torch.from_numpy(rows).to(DEV)
-    xs_h = [x.index_select(0, idx).cpu() for x in d["inputs"]]
-    q_ref, s_ref, h_ref = orc.arnfp8([_bits(x) for x in xs_h], _bits(d["gamma"].cpu()), w.eps,
-                                     w.weight_offset, w.scale_ub,
-                                     residual_in=_bits(res0.index_select(0, idx).cpu()))
-    assert_bits_equal(_bits(res_out.index_select(0, idx)), h_ref, "residual_out")
-    assert_scales_close(scales.index_select(0, idx).cpu().numpy(), s_ref)
-    assert_fp8_close(_fp8(out.index_select(0, idx)), q_ref)
-    clamp = np.float32(w.scale_ub / 448.0)
-    assert (s_ref == clamp).sum() > 0, "the sample should contain rows where scale_ub clamps"
-    # every row: scales within [floor, ub/448]; every row reaches +-448
-    s_all = scales.cpu().numpy()
-    assert np.all(s_all <= clamp) and np.all(s_all >= np.float32(1.0 / 229376.0))
-    mags = (out.view(torch.uint8) & 0x7F).amax(dim=1).cpu().numpy()
-    assert np.all(mags == 0x7E)
-
-
 P2_COLS = [8, 2880, 7168, 7176, 8192, 16384]
 P2_ROWS = [1, 32, 37, 64]
 
@@ -566,37 +538,3 @@ def test_concurrent_calls_on_two_streams(arn, synth):
     for k in range(2):
         for got, want in zip(sets[k][1:], ref[k]):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), k
-
-
-@pytest.mark.parametrize("rank", [0, 5, 7])
-def test_two_stage_share_on_the_full_prefill_workload(arn, orc, synth, rank):
-    """One rank's share of the full prefill workload (8 ranks, 1024 rows each),
-    as the benchmark times it: seeded sampled rows of the staging slot and of
-    the residual against the oracle."""
-    import oracle as orc_mod
-
-    w = synth.WORKLOADS["prefill_p8_8192x7168"]
-    ngpus = 8
-    print(f"[share] full prefill, rank {rank} of {ngpus}", flush=True)
-    d = synth.make_inputs(w, device=DEV)
-    nbytes = arn.arnfp8_stage_bytes(w.rows, w.cols, ngpus)
-    staging = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
-    res_out = torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=DEV)
-    arn.arnfp8_run_share(d["inputs"], d["residual"], res_out, staging, d["gamma"], w.eps,
-                         w.weight_offset, w.scale_ub, ngpus=ngpus, rank=rank)
-    torch.cuda.synchronize()
-    first, count = orc_mod.share_rows(w.rows, ngpus, rank)
-    S = -(-w.rows // ngpus)
-    local = np.unique(np.concatenate([[0, count - 1],
-                                      np.random.default_rng(rank).choice(count, 62, replace=False)]))
-    idx = torch.from_numpy(first + local).to(DEV)
-    xs_h = [x.index_select(0, idx).cpu() for x in d["inputs"]]
-    q, s, h = orc.arnfp8([_bits(x) for x in xs_h], _bits(d["gamma"].cpu()), w.eps,
-                         w.weight_offset, w.scale_ub,
-                         residual_in=_bits(d["residual"].index_select(0, idx).cpu()))
-    got = staging.cpu().numpy()
-    data = got[: S * w.cols].reshape(S, w.cols)
-    scales = got[S * w.cols: S * w.cols + 4 * S].view(np.float32)
-    assert_fp8_close(data[local], q)
-    assert_scales_close(scales[local], s)
-    assert_bits_equal(_bits(res_out.index_select(0, idx)), h, "share residual")
