@@ -17,6 +17,10 @@ SOURCES = [os.path.join(PKG, "csrc", f) for f in
            ("arnfp8.hip", "arnfp8_rows_e4m3.hip", "arnfp8_rows_e5m2.hip", "arnfp8_rows_mxfp8.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libarnfp8.so")
+# Achievable-bandwidth reference kernels for the benchmark, in a library of
+# their own (not part of the product library).
+REF_SOURCES = [os.path.join(PKG, "csrc", "arnfp8_ref_kernels.hip")]
+REF_LIB_PATH = os.path.join(PKG, "libarnfp8_ref.so")
 ARCH = os.environ.get("ARNFP8_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -36,26 +40,29 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link ``all_reduce_rmsnorm_amd/libarnfp8.so``."""
+    """Compile every HIP source for gfx950 and link ``all_reduce_rmsnorm_amd/libarnfp8.so``
+    (and the benchmark's reference kernels, ``libarnfp8_ref.so``)."""
     obj_dir = os.path.join(PKG, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    procs, objs = [], []
-    for src in SOURCES:
+    procs, objs = [], {}
+    for src in SOURCES + REF_SOURCES:
         obj = os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o")
         cmd = [hipcc(), *HIPCC_FLAGS, "-c", f"-I{INCLUDE}", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((subprocess.Popen(cmd), src))
-        objs.append(obj)
+        objs[src] = obj
     failed = [src for p, src in procs if p.wait() != 0]
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB_PATH + ".tmp"
-    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(link), flush=True)
-    subprocess.run(link, check=True)
-    os.replace(tmp, LIB_PATH)
+    for srcs, path in ((SOURCES, LIB_PATH), (REF_SOURCES, REF_LIB_PATH)):
+        tmp = path + ".tmp"
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                *[objs[s] for s in srcs], "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -119,15 +119,33 @@ struct RowConfig {
 
 // Smallest chunks-per-lane (1, 2, 4, 8, 16) that fits the row in at most 512
 // lanes.  Lanes are rounded up to whole waves, except that batches smaller
-// than four rows per CU use all 512 lanes when a lane holds two or more
-// chunks.  Measured on MI355X for 7168-wide rows: 512 x 2 beats 448 x 2 by
-// ~3 % at 1-128 rows (and 1024 x 1 everywhere); 448 x 2 beats 512 x 2 by
-// ~1 % at 8192 rows.  Row outputs use nt stores (the fastest policy when
-// the output buffers are not cache-resident, at every batch size measured).
-RowConfig pick_row_config(int64_t rows, int c16) {
+// than 32 rows per CU use all 512 lanes when a lane holds two or more
+// chunks.  Measured on MI355X for 7168-wide rows, P = 8, inputs out of
+// cache, graph replay: 512 x 2 against 448 x 2 is 9.78 / 9.90 us at 256 rows,
+// 28.5 / 28.9 us at 1024, 54.1 / 55.9 us at 2048, 104.0 / 104.7 us at 4096
+// and 178.2 / 179.2 us at 7168; at 8192 rows the two are level under graph
+// replay and 448 x 2 is ~1 % faster back to back.  Four chunks per lane (256
+// lanes, also with four workgroups per CU resident) and one (896 lanes) are
+// slower at every batch from 256 rows up.  Row outputs use nt stores (the
+// fastest policy when the output buffers are not cache-resident, at every
+// batch size measured).
+// With eight slabs and at most one row per CU, one chunk per lane (up to 1024
+// lanes) is faster: measured (graph replay, inputs out of cache / the same
+// inputs every call) at 1 row 5.71 / 3.75 against 5.89 / 3.90 us for
+// 7168-wide rows and 5.84 / 3.75 against 6.08 / 3.89 us for 8192-wide rows,
+// and 2-3 % faster out of cache up to 256 rows.  With four slabs it is not
+// (1 row: 5.02 / 3.44 against 4.97 / 3.22 us).
+RowConfig pick_row_config(int64_t rows, int c16, int P) {
   static const int vpts[5] = {1, 2, 4, 8, 16};
-  const bool small_batch = rows < 4 * (int64_t)device_cus();
+  const int64_t cus = device_cus();
+  const bool small_batch = rows < 32 * cus;
   RowConfig cfg{512, 16, 1, 0};
+  if (P >= 8 && rows <= cus && c16 <= 1024) {
+    cfg.vpt = 1;
+    cfg.threads = (c16 + 63) / 64 * 64;
+    cfg.grid = (int)rows;
+    return cfg;
+  }
   for (int i = 0; i < 5; ++i) {
     const int lanes = (c16 + vpts[i] - 1) / vpts[i];
     if (lanes <= 512) {
@@ -198,10 +216,10 @@ int prepare_fused(const void *const *inputs, const void *residual_in, void *resi
 // Resolves the launch options against the automatic choice.  The options are
 // checked first; the device is queried only when lanes and chunks per lane
 // are both left automatic.
-int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfig *cfg) {
+int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, int P, RowConfig *cfg) {
   static const int vpts[5] = {1, 2, 4, 8, 16};
   if (opt == nullptr) {
-    *cfg = pick_row_config(rows, c16);
+    *cfg = pick_row_config(rows, c16, P);
     return ARNFP8_OK;
   }
   if (opt->variant != ARNFP8_VARIANT_AUTO && opt->variant != ARNFP8_VARIANT_ROW)
@@ -227,7 +245,7 @@ int resolve_row_config(const arnfp8_launch *opt, int64_t rows, int c16, RowConfi
     cfg->vpt = opt->vpt;
     cfg->threads = ((c16 + cfg->vpt - 1) / cfg->vpt + 63) / 64 * 64;
   } else {
-    *cfg = pick_row_config(rows, c16);
+    *cfg = pick_row_config(rows, c16, P);
   }
   // One chunk per lane allows up to 1024 lanes; more chunks per lane, 512.
   if (cfg->threads > (cfg->vpt == 1 ? 1024 : 512)) return ARNFP8_BAD_CONFIG;
@@ -294,7 +312,7 @@ extern "C" int arnfp8_run_fmt(const void *const *inputs, const void *residual_in
                      weight_offset, scale_ub, rows, cols, P, &a, out_format);
   if (st != ARNFP8_OK) return st;
   RowConfig cfg;  // after validation: the automatic choice queries the device
-  st = resolve_row_config(opt, rows, (int)(cols / 8), &cfg);
+  st = resolve_row_config(opt, rows, (int)(cols / 8), P, &cfg);
   if (st != ARNFP8_OK) return st;
   return launch(row_table(out_format, P, cfg.vpt, residual_in != nullptr, residual_out != nullptr,
                           cfg.sc1_stores != 0),
@@ -377,7 +395,7 @@ extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_
                      cols, P, &a);
   if (st != ARNFP8_OK) return st;
   RowConfig cfg;
-  st = resolve_row_config(nullptr, count, (int)(cols / 8), &cfg);
+  st = resolve_row_config(nullptr, count, (int)(cols / 8), P, &cfg);
   if (st != ARNFP8_OK) return st;
   return launch(row_table(ARNFP8_FMT_E4M3FN, P, cfg.vpt, residual_in != nullptr,
                           residual_out != nullptr, cfg.sc1_stores != 0),

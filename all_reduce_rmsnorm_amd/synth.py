@@ -40,6 +40,7 @@ class Workload:
     outlier_mult: float = 1.0   # ... by this factor, the same positions in every slab
     sum_only: bool = False
     seed: int = 0
+    in_place: bool = False      # the residual is updated in place (residual_out == residual_in)
     notes: str = field(default="", compare=False)
 
     @property
@@ -68,12 +69,18 @@ WORKLOADS = {
                  gamma_law=("uniform", 1.0, 1.0), sum_only=True),
         Workload("decode_p4_32x7168", P=4, rows=32, cols=7168, x_std=0.5, residual_std=1.0,
                  gamma_law=("uniform", 0.8, 1.2), weight_offset=0.0, eps=1e-6, scale_ub=1200.0,
-                 notes="residual updated in place"),
+                 in_place=True, notes="residual updated in place"),
         Workload("unit_offset_p8_128x8192", P=8, rows=128, cols=8192, x_std=0.25, residual_std=1.0,
                  gamma_law=("normal", 0.0, 0.02), weight_offset=1.0, eps=1e-5, scale_ub=1200.0),
         Workload("prefill_p8_8192x7168", P=8, rows=8192, cols=7168, x_std=0.5, residual_std=1.0,
                  gamma_law=("uniform", 0.8, 1.2), weight_offset=0.0, eps=1e-6, scale_ub=64.0,
                  outlier_frac=0.001, outlier_mult=100.0),
+        Workload("token_p4_1x7168", P=4, rows=1, cols=7168, x_std=0.5, residual_std=1.0,
+                 gamma_law=("uniform", 0.8, 1.2), weight_offset=0.0, eps=1e-6, scale_ub=1200.0,
+                 in_place=True, notes="one token with the decode workload's laws; residual updated in place"),
+        Workload("token_p8_1x8192", P=8, rows=1, cols=8192, x_std=0.25, residual_std=1.0,
+                 gamma_law=("normal", 0.0, 0.02), weight_offset=1.0, eps=1e-5, scale_ub=1200.0,
+                 notes="one token with the unit-offset workload's laws"),
         Workload("prefill_share_p8_1024x7168", P=8, rows=1024, cols=7168, x_std=0.5, residual_std=1.0,
                  gamma_law=("uniform", 0.8, 1.2), weight_offset=0.0, eps=1e-6, scale_ub=64.0,
                  outlier_frac=0.001, outlier_mult=100.0,

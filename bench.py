@@ -10,22 +10,27 @@ outputs in cache.  Prints ONE JSON line:
 
   value       algorithmic HBM bytes per step / wall time per step   (GB/s)
   roofline    the kernel's algorithmic bytes / its average duration from HIP
-              events on the launch stream, against the 8 TB/s HBM peak; the
+              events on the launch stream (also the median of 5 equal
+              segments of the timed steps), against the 8 TB/s HBM peak; the
               measured HBM traffic (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
               by a plain copy of known size) when a committed counter summary
               matches the current kernel source
   cpu_baseline the CPU oracle on the same bytes (rows of the same workload)
-  latency_us_per_call  graph-replayed microseconds per call for the decode
-              shapes (P = 4 [32, 7168], P = 8 [128, 8192], P = 2 [4, 256]) and of
-              the sum alone (P = 4 [64, 4096]), the
-              same buffers every call (cache-warm); latency_us_per_call_cold
-              the same with every call reading its own inputs, > 512 MB in all
+  two_stage_share  the 8 ranks' 1024-row shares of the same inputs, replayed
+              from a captured graph (no host launch cost), with its roofline
+  latency     per small workload (decode, unit offset, one token, tiny, sum):
+              graph-replayed microseconds per call with the same buffers every
+              call (cache-warm) and with every call on its own inputs after a
+              1 GiB cache flush (cold), the single-call graph latency, and the
+              kernel-only duration from the committed kernel trace
+  reference_kernels  a plain copy, the sum alone, and the fused kernel's byte
+              mix without its arithmetic (read-only, write-only, traffic twin)
 
-Other modes (not the JSON contract): ``--workload NAME`` times another
-workload; ``--pmc-calib`` first runs one plain copy of known size (the P = 1
-sum kernel; it scales the HBM counters); ``--summarize-pmc DIR`` turns rocprofv3 counter CSVs into the
-committed summary; ``--summarize-ktrace DIR`` does the same for a
-``rocprofv3 --kernel-trace --stats`` run.
+Other modes (not the JSON contract): ``--profile-workload NAME`` runs only that
+workload's calls (for rocprofv3); ``--pmc-calib`` first runs one plain copy of
+known size (the P = 1 sum kernel; it scales the HBM counters);
+``--summarize-pmc DIR`` and ``--summarize-ktrace DIR`` turn rocprofv3 output
+into the committed summaries under profiles/.
 """
 from __future__ import annotations
 
@@ -45,13 +50,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 DEFAULT_WORKLOAD = "prefill_p8_8192x7168"
-DECODE_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "tiny_p2_4x256",
-                    "sum_p4_64x4096"]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
+SHARE_WORKLOAD = "prefill_share_p8_1024x7168"
+SHARE_NGPUS = 8
+LATENCY_WORKLOADS = ["decode_p4_32x7168", "unit_offset_p8_128x8192", "token_p4_1x7168",
+                     "token_p8_1x8192", "tiny_p2_4x256", "sum_p4_64x4096"]
+PROFILES = os.path.join(ROOT, "profiles")
 # The device code, the host code that picks its launch shape and cache
-# policy, the ABI header whose constants both use, and the build flags: the
-# committed HBM-counter summary applies only while their code (comments
-# aside) is unchanged.
+# policy, the ABI header whose constants both use, and the build flags: a
+# committed profile summary applies only while their code (comments aside)
+# is unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_kernels.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_tables.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8.hip"),
@@ -59,9 +66,25 @@ KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_k
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
 
 
+def kernel_name_of(workload) -> str:
+    """The kernel a workload times: the sum kernel for the sum-only workload,
+    else the fused row kernel."""
+    from all_reduce_rmsnorm_amd import synth
+
+    return "arn_sum_kernel" if synth.WORKLOADS[workload].sum_only else "arnfp8_row_kernel"
+
+
+def profile_path(workload: str, kind: str) -> str:
+    """profiles/<kernel>_<workload>_<kind>.md, kind "hbm_traffic" or "kernel_trace"."""
+    return os.path.join(PROFILES, f"{kernel_name_of(workload)}_{workload}_{kind}.md")
+
+
+PMC_SUMMARY = os.path.join(PROFILES, "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
+
+
 def _code_only(path: str) -> bytes:
     """The file with comments and blank space removed, so that an edit of a
-    comment does not retire the counters taken on the code."""
+    comment does not retire the profiles taken on the code."""
     with open(path, encoding="utf-8") as f:
         text = f.read()
     if path.endswith(".py"):
@@ -83,6 +106,28 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+# ------------------------------------------------------ committed profiles --
+
+def read_profile(path: str, key: str, kernel_hash: str):
+    """The number after ``key:`` in a committed profile summary, or None when
+    the summary is missing or was taken on different kernel source."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_val = re.search(rf"(?m)^{re.escape(key)}:\s*([0-9.eE+-]+)\s*$", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_hash:
+        return None
+    v = float(m_val.group(1))
+    return int(v) if v.is_integer() else v
+
+
+def read_traffic(kernel_hash: str, path: str | None = None):
+    """HBM bytes per launch from a committed counter summary (None if stale)."""
+    return read_profile(PMC_SUMMARY if path is None else path, "traffic_bytes_per_launch",
+                        kernel_hash)
+
+
 # --------------------------------------------------------------- GPU side --
 
 # Outputs rotate over enough buffer sets that together they exceed twice the
@@ -97,26 +142,50 @@ def out_sets_for(w) -> int:
     return max(1, min(MAX_OUT_SETS, -(-CACHE_FLUSH_BYTES // max(1, per))))
 
 
+def _outputs(w, torch, dev, rows):
+    o = {"out": None, "scales": None, "res_out": None, "sum_out": None}
+    if w.sum_only:
+        o["sum_out"] = torch.empty((rows, w.cols), dtype=torch.bfloat16, device=dev)
+    else:
+        o["out"] = torch.empty((rows, w.cols), dtype=torch.float8_e4m3fn, device=dev)
+        o["scales"] = torch.empty((rows,), dtype=torch.float32, device=dev)
+        if w.residual_std is not None:
+            o["res_out"] = torch.empty((rows, w.cols), dtype=torch.bfloat16, device=dev)
+    return o
+
+
 def alloc_workload(w, torch, dev, out_sets: int = 1, seed=None):
     """Inputs of workload `w` on `dev`, and `out_sets` sets of output buffers
-    (d["outs"]; d["out"], d["scales"], d["res_out"], d["sum_out"] are set 0)."""
+    (d["outs"]; d["out"], d["scales"], d["res_out"], d["sum_out"] are set 0).
+    The residual is written out of place, so that every step is identical."""
     from all_reduce_rmsnorm_amd import synth
 
     d = synth.make_inputs(w, device=dev, seed=seed)
-    rows, cols = w.rows, w.cols
-    d["outs"] = []
-    for _ in range(out_sets):
-        o = {"out": None, "scales": None, "res_out": None, "sum_out": None}
-        if w.sum_only:
-            o["sum_out"] = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-        else:
-            o["out"] = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=dev)
-            o["scales"] = torch.empty((rows,), dtype=torch.float32, device=dev)
-            if d["residual"] is not None:
-                o["res_out"] = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-        d["outs"].append(o)
+    d["outs"] = [_outputs(w, torch, dev, w.rows) for _ in range(out_sets)]
     d.update(d["outs"][0])
     return d
+
+
+def alloc_windows(w, torch, dev, nwin: int):
+    """`nwin` disjoint copies ("windows") of workload `w`'s inputs and outputs,
+    cut from one tensor set of nwin * rows rows drawn by the same recipe: a
+    call on window k touches bytes no other window touches.  A workload whose
+    residual is updated in place writes it back into its own window."""
+    from all_reduce_rmsnorm_amd import synth
+
+    big = synth.make_inputs(w, device=dev, rows=nwin * w.rows)
+    outs = _outputs(w, torch, dev, nwin * w.rows)
+    wins = []
+    for k in range(nwin):
+        sl = slice(k * w.rows, (k + 1) * w.rows)
+        d = {"inputs": [x[sl] for x in big["inputs"]], "gamma": big["gamma"],
+             "residual": None if big["residual"] is None else big["residual"][sl]}
+        for key, t in outs.items():
+            d[key] = None if t is None else t[sl]
+        if w.in_place and d["residual"] is not None:
+            d["res_out"] = d["residual"]
+        wins.append(d)
+    return wins
 
 
 def input_sha256(d, torch) -> str:
@@ -138,86 +207,209 @@ def rotating(fns):
     return lambda: next(it)()
 
 
+def call_on(w, d, arn, launch=None):
+    """One call of workload `w` on the buffers of `d` (d["out"] etc.)."""
+    if w.sum_only:
+        return lambda: arn.arn_sum_bf16(d["inputs"], d["sum_out"])
+    if launch is not None:
+        return lambda: arn.arnfp8_run_ex(d["inputs"], d["residual"], d["res_out"], d["out"],
+                                         d["scales"], d["gamma"], w.eps, w.weight_offset,
+                                         w.scale_ub, launch=launch)
+    return lambda: arn.arnfp8_run(d["inputs"], d["residual"], d["res_out"], d["out"],
+                                  d["scales"], d["gamma"], w.eps, w.weight_offset, w.scale_ub)
+
+
 def step_fn(w, d, arn):
     """One step of workload `w`, each call writing the next output set."""
-    def one(o):
-        if w.sum_only:
-            return lambda: arn.arn_sum_bf16(d["inputs"], o["sum_out"])
-        return lambda: arn.arnfp8_run(d["inputs"], d["residual"], o["res_out"], o["out"],
-                                      o["scales"], d["gamma"], w.eps, w.weight_offset, w.scale_ub)
-    return rotating([one(o) for o in d["outs"]])
+    return rotating([call_on(w, dict(d, **o), arn) for o in d["outs"]])
 
 
-def time_steps(torch, fn, steps, warmup):
+def share_calls(w, d, arn, staging):
+    """The SHARE_NGPUS ranks' two-stage shares of the prefill inputs `d`, each
+    into its own staging slot, the residual rows written into d["res_out"]."""
+    return [(lambda r=r: arn.arnfp8_run_share(d["inputs"], d["residual"], d["res_out"],
+                                              staging[r], d["gamma"], w.eps, w.weight_offset,
+                                              w.scale_ub, ngpus=SHARE_NGPUS, rank=r))
+            for r in range(SHARE_NGPUS)]
+
+
+def share_bytes(w) -> int:
+    """Algorithmic bytes of one rank's share of workload `w` (all its rows'
+    traffic; the slot holds the share's fp8 rows and scales)."""
+    rows = -(-w.rows // SHARE_NGPUS)
+    return (2 * w.P + 4 + 1) * rows * w.cols + 4 * rows + 2 * w.cols
+
+
+def time_steps(torch, fn, steps, warmup, segments=1):
     """Exactly `steps` calls, synchronised on both sides: (wall ms per step,
-    ms per launch from one HIP event pair on the launch stream around the
-    same `steps` launches, which run back to back)."""
+    ms per launch from a HIP event pair on the launch stream around the same
+    `steps` launches, which run back to back, [ms per launch of each of
+    `segments` equal segments of them, from events between the segments])."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bounds = [round(i * steps / segments) for i in range(segments + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in bounds]
     t0 = time.perf_counter()
-    a.record(stream)
-    for _ in range(steps):
-        fn()
-    b.record(stream)
+    ev[0].record(stream)
+    for i in range(segments):
+        for _ in range(bounds[i + 1] - bounds[i]):
+            fn()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall / steps * 1e3, a.elapsed_time(b) / steps
+    segs = [ev[i].elapsed_time(ev[i + 1]) / max(1, bounds[i + 1] - bounds[i])
+            for i in range(segments)]
+    return wall / steps * 1e3, ev[0].elapsed_time(ev[-1]) / steps, segs
 
 
-def graph_us_per_call_cold(torch, w, arn, dev, min_bytes=600 << 20, max_sets=400):
-    """Microseconds per call with every call in the captured graph reading its
-    own input set, the sets together larger than the 256 MB Infinity Cache."""
-    from all_reduce_rmsnorm_amd import synth
-
-    per = w.algorithmic_bytes()
-    nsets = int(min(max_sets, -(-min_bytes // per)))
-    if nsets * per < min_bytes:
-        return None, nsets
-    base = alloc_workload(w, torch, dev)
-    sets = []
-    for k in range(nsets):
-        dk = dict(base)
-        dk["inputs"] = [x.clone() for x in base["inputs"]]
-        o = {key: (None if t is None else torch.empty_like(t)) for key, t in base["outs"][0].items()}
-        if base["residual"] is not None:
-            dk["residual"] = base["residual"].clone()
-            o["res_out"] = dk["residual"]  # in place, as the decode workloads update it
-        dk["outs"] = [o]
-        sets.append(step_fn(w, dk, arn))
-    us = graph_us_per_call(torch, lambda: [f() for f in sets], calls=1, reps=5) / nsets
-    del sets, base
-    torch.cuda.empty_cache()
-    return us, nsets
+def median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
 
 
-def graph_us_per_call(torch, fn, calls=100, reps=5):
-    """Microseconds per call with `calls` calls captured in one graph."""
+def graph_us_per_call(torch, fns, reps=7, flush=None):
+    """Median microseconds per call of the calls `fns`, captured in order in
+    one graph and replayed `reps` times; each replay is timed alone by a HIP
+    event pair.  With `flush` (a device buffer), the buffer is overwritten
+    and the device synchronised before every replay, so the replay starts
+    with no input in any cache."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for _ in range(3):
-            fn()
+        for f in fns[:3]:
+            f()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(calls):
-            fn()
+        for f in fns:
+            f()
     g.replay()
     torch.cuda.synchronize()
-    best = []
+    times = []
     for _ in range(reps):
+        if flush is not None:
+            flush.fill_(0x5A)
+            torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         g.replay()
         b.record()
         torch.cuda.synchronize()
-        best.append(a.elapsed_time(b) * 1e3 / calls)
-    best.sort()
-    return best[len(best) // 2]
+        times.append(a.elapsed_time(b) * 1e3 / len(fns))
+    del g
+    return median(times)
+
+
+def latency_figures(w, torch, arn, dev, flush, khash, calls=100, nwin=64):
+    """Graph-replayed microseconds per call of small workload `w`."""
+    wins = alloc_windows(w, torch, dev, nwin)
+    fs = [call_on(w, d, arn) for d in wins]
+    alg = w.algorithmic_bytes()
+    r = {"warm_us_per_call": graph_us_per_call(torch, [fs[0]] * calls),
+         "cold_us_per_call": graph_us_per_call(torch, fs, flush=flush),
+         "single_call_graph_us_warm": graph_us_per_call(torch, [fs[0]], reps=21),
+         "single_call_graph_us_cold": graph_us_per_call(torch, [fs[1]], reps=21, flush=flush)}
+    r = {k: round(v, 3) for k, v in r.items()}
+    r["algorithmic_bytes"] = alg
+    r["gbs_warm"] = round(alg / (r["warm_us_per_call"] * 1e-6) / 1e9, 1)
+    r["gbs_cold"] = round(alg / (r["cold_us_per_call"] * 1e-6) / 1e9, 1)
+    r["residual"] = ("in place" if w.in_place else "out of place") if w.residual_std else None
+    k_us = read_profile(profile_path(w.name, "kernel_trace"), "mean_us", khash)
+    traffic = read_profile(profile_path(w.name, "hbm_traffic"), "traffic_bytes_per_launch", khash)
+    r["kernel_us_trace"] = k_us
+    r["frac_kernel_trace"] = (round(alg / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                              if k_us else None)
+    r["traffic"] = traffic
+    if not w.sum_only and w.rows == 1:
+        # One token: the automatic launch shape against one chunk per lane
+        # (a workgroup of up to 1024 lanes), both cold.
+        fs1 = [call_on(w, d, arn, launch={"vpt": 1}) for d in wins]
+        r["one_chunk_per_lane_cold_us_per_call"] = round(
+            graph_us_per_call(torch, fs1, flush=flush), 3)
+    del wins, fs
+    torch.cuda.empty_cache()
+    return r
+
+
+# -------------------------------------------------- reference kernels ------
+
+_ref = None
+
+
+def ref_library():
+    """libarnfp8_ref.so: the benchmark's achievable-bandwidth reference kernels."""
+    global _ref
+    if _ref is None:
+        import ctypes
+
+        path = os.path.join(ROOT, "all_reduce_rmsnorm_amd", "libarnfp8_ref.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run `python -m all_reduce_rmsnorm_amd.build`")
+        L = ctypes.CDLL(path)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.arnref_read.argtypes = [ctypes.POINTER(vp), ci, vp, i64, i64, ci, ci, vp]
+        L.arnref_write.argtypes = [ctypes.POINTER(vp), ci, i64, i64, ci, ci, vp]
+        L.arnref_twin.argtypes = [ctypes.POINTER(vp), ci, vp, vp, i64, i64, ci, ci, vp]
+        for f in (L.arnref_read, L.arnref_write, L.arnref_twin):
+            f.restype = ci
+        _ref = L
+    return _ref
+
+
+def reference_kernels(w, d, torch, arn, dev, s_bufs, steps=20):
+    """Bandwidth of kernels that move the fused kernel's bytes, on the same
+    device, inputs and launch pattern (one workgroup per row)."""
+    import ctypes
+
+    L = ref_library()
+    stream = torch.cuda.current_stream().cuda_stream
+    row_bytes = 2 * w.cols
+    arr = lambda ts: (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+    def checked(st):
+        if st != 0:
+            raise RuntimeError(f"reference kernel launch failed with status {st}")
+
+    out = {}
+    src = torch.ones((65536, 8192), dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    _, cp_k, _ = time_steps(torch, lambda: arn.arn_sum_bf16([src], dst), 10, 3)
+    out["copy_1GiB_gbs"] = round(2 * (1 << 30) / (cp_k * 1e-3) / 1e9, 1)
+    del src, dst
+    _, sm_k, _ = time_steps(torch, rotating([(lambda sb=sb: arn.arn_sum_bf16(d["inputs"], sb))
+                                             for sb in s_bufs]), 10, 3)
+    out["sum_only_same_slabs_gbs"] = round((2 * w.P + 2) * w.numel / (sm_k * 1e-3) / 1e9, 1)
+    streams = list(d["inputs"]) + [d["residual"]]
+    sink = torch.empty((w.rows, 16), dtype=torch.uint8, device=dev)
+    rd = arr(streams)
+    _, rd_k, _ = time_steps(torch, lambda: checked(L.arnref_read(rd, len(streams), sink.data_ptr(),
+                                                                 w.rows, row_bytes, 0, 0, stream)),
+                            steps, 3)
+    rd_bytes = len(streams) * w.numel * 2
+    out["read_only_streams"] = len(streams)
+    out["read_only_gbs"] = round(rd_bytes / (rd_k * 1e-3) / 1e9, 1)
+    wsets = [torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=dev) for _ in range(8)]
+    wptrs = [arr([t]) for t in wsets]
+    _, wr_k, _ = time_steps(torch, rotating([(lambda p=p: checked(L.arnref_write(
+        p, 1, w.rows, row_bytes, 0, 0, stream))) for p in wptrs]), steps, 3)
+    out["write_only_gbs"] = round(w.numel * 2 / (wr_k * 1e-3) / 1e9, 1)
+    del wsets
+    # The twin: the same 9 read streams, 16 + 8 bytes written per 16-byte
+    # chunk into the fused step's own rotating output sets.
+    tw = [(lambda o=o: checked(L.arnref_twin(rd, len(streams), o["res_out"].data_ptr(),
+                                             o["out"].data_ptr(), w.rows, row_bytes, 0, 0,
+                                             stream))) for o in d["outs"]]
+    _, tw_k, _ = time_steps(torch, rotating(tw), steps, 3)
+    tw_bytes = rd_bytes + 3 * w.numel
+    out["traffic_twin_us"] = round(tw_k * 1e3, 2)
+    out["traffic_twin_gbs"] = round(tw_bytes / (tw_k * 1e-3) / 1e9, 1)
+    out["note"] = ("read/write kernels of libarnfp8_ref.so: one workgroup per row, 16-byte "
+                   "non-temporal loads and stores, no arithmetic; twin = the fused kernel's "
+                   "byte mix (9 read streams, 16 + 8 bytes written per chunk)")
+    return out
 
 
 # -------------------------------------------------------------- CPU side ---
@@ -337,28 +529,26 @@ def cpu_oracle_threaded(w, d, torch, passes=3, max_threads=16):
 
 # ------------------------------------------------------- HBM counters ------
 
-def read_traffic(kernel_hash: str):
-    """(bytes per launch, note) from the committed counter summary, or None
-    when it is missing or was taken on different kernel source."""
-    if not os.path.exists(PMC_SUMMARY):
-        return None
-    text = open(PMC_SUMMARY).read()
-    m_hash = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash:
-        return None
-    return int(m_bytes.group(1))
+def _kernel_filter(workload):
+    """A predicate on rocprofv3 kernel names: the kernel `workload` times
+    (the e4m3fn row kernel with its P, or the sum kernel with its P)."""
+    from all_reduce_rmsnorm_amd import synth
+
+    w = synth.WORKLOADS[workload]
+    want = f"arn_sum_kernel<{w.P}," if w.sum_only else f"arnfp8_row_kernel<0, {w.P},"
+    return lambda name: want in name.replace("(anonymous namespace)::", "")
 
 
-def summarize_pmc(directory: str, out_path: str, workload: str):
+def summarize_pmc(directory: str, out_path: str, workload: str, command: str = ""):
     """Build the counter summary from rocprofv3 --pmc CSV output under `directory`:
-    one run with FETCH_SIZE, one with WRITE_SIZE, each holding the fused kernel's
-    dispatches and one plain copy of known size (``--pmc-calib``)."""
+    one run with FETCH_SIZE, one with WRITE_SIZE, each holding the workload's
+    kernel dispatches and one plain copy of known size (``--pmc-calib``)."""
     import csv
 
     from all_reduce_rmsnorm_amd import synth
 
     w = synth.WORKLOADS[workload]
+    is_kernel = _kernel_filter(workload)
     per = {}  # counter -> {"kernel": [kib...], "copy": [kib...]}
     files = sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True))
     if not files:
@@ -368,8 +558,7 @@ def summarize_pmc(directory: str, out_path: str, workload: str):
             name = row.get("Kernel_Name", "")
             ctr = row.get("Counter_Name", "")
             val = float(row.get("Counter_Value", "nan"))
-            kind = "kernel" if "arnfp8_row_kernel" in name else (
-                "copy" if "arn_sum_kernel<1" in name else None)
+            kind = "kernel" if is_kernel(name) else ("copy" if "arn_sum_kernel<1, 4>" in name else None)
             if kind is None or ctr not in ("FETCH_SIZE", "WRITE_SIZE"):
                 continue
             per.setdefault(ctr, {}).setdefault(kind, []).append(val)
@@ -386,31 +575,32 @@ def summarize_pmc(directory: str, out_path: str, workload: str):
         factor = calib_bytes / (c_kib * 1024.0)
         scaled = k_kib * 1024.0 * factor
         total += scaled
-        lines.append(f"| {ctr} | {k_kib:.0f} KiB ({len(k)} dispatches) | {c_kib:.0f} KiB | "
-                     f"{factor:.4f} | {scaled / 1e6:.2f} MB |")
-    alg = w.algorithmic_bytes()
+        lines.append(f"| {ctr} | {k_kib:.1f} KiB ({len(k)} dispatches) | {c_kib:.0f} KiB | "
+                     f"{factor:.4f} | {scaled / 1e6:.3f} MB |")
+    alg = share_bytes(w) if workload == SHARE_WORKLOAD else w.algorithmic_bytes()
+    if not command:
+        command = (f"python -u bench.py --profile-workload {workload} --pmc-calib")
     text = "\n".join([
-        f"# HBM traffic of the fused row kernel on {w.name}",
+        f"# HBM traffic of `{kernel_name_of(workload)}` on {workload}",
         "",
         "Counters from two `rocprofv3 --pmc` runs (FETCH_SIZE, then WRITE_SIZE), per",
         "dispatch, scaled by what the same counter reads for a plain copy of",
-        f"{calib_bytes} bytes (read {calib_bytes} B, write {calib_bytes} B).",
+        f"{calib_bytes} bytes (read {calib_bytes} B, write {calib_bytes} B): the P = 1 sum kernel.",
         "Commands (from the repository root, on one MI355X):",
         "",
-        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/pmc_fetch -o fetch -- "
-        "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-latency --pmc-calib",
-        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {directory}/pmc_write -o write -- "
-        "python -u bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-latency --pmc-calib",
-        f"    python bench.py --summarize-pmc {directory}",
+        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/pmc_fetch -o fetch -- {command}",
+        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {directory}/pmc_write -o write -- {command}",
+        f"    python bench.py --summarize-pmc {directory} --workload {workload}",
         "",
-        "| counter | fused kernel (mean per dispatch) | copy kernel | scale factor | scaled bytes |",
+        "| counter | kernel (mean per dispatch) | copy kernel | scale factor | scaled bytes |",
         "|---|---|---|---|---|",
         *lines,
         "",
+        f"workload: {workload}",
         f"kernel_source_hash: {kernel_source_hash()}",
         f"traffic_bytes_per_launch: {int(round(total))}",
         f"algorithmic_bytes_per_launch: {alg}",
-        f"traffic / algorithmic: {total / alg:.4f}",
+        f"traffic_over_algorithmic: {total / alg:.4f}",
         "",
     ])
     with open(out_path, "w") as f:
@@ -425,12 +615,16 @@ def _short_name(name: str) -> str:
     return name.split("(")[0]
 
 
-def summarize_ktrace(directory: str, out_path: str, command: str):
+def summarize_ktrace(directory: str, out_path: str, command: str, workload: str):
     """Summarise a rocprofv3 --kernel-trace --stats CSV run: the library's
-    kernels, split by launch shape (grid, workgroup), with mean durations."""
+    kernels, split by launch shape (grid, workgroup), with mean durations;
+    the workload's own kernel and launch shape get machine-readable lines."""
     import csv
     from collections import defaultdict
 
+    from all_reduce_rmsnorm_amd import synth
+
+    w = synth.WORKLOADS[workload]
     traces = sorted(glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True))
     stats = sorted(glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True))
     if not traces:
@@ -439,20 +633,19 @@ def summarize_ktrace(directory: str, out_path: str, command: str):
     for f in traces:
         for r in csv.DictReader(open(f)):
             name = r["Kernel_Name"]
-            if "arnfp8_" not in name and "arn_sum_kernel" not in name:
+            if "arnfp8_" not in name and "arn_sum_kernel" not in name and "arnref" not in name:
                 continue
-            key = (_short_name(name),
-                   int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            key = (_short_name(name), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
             shapes[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines = [f"# Kernel trace: {os.path.basename(out_path)[:-3]}", "",
+    lines = [f"# Kernel trace: `{kernel_name_of(workload)}` on {workload}", "",
              "Command (from the repository root, on one MI355X):", "",
              f"    {command}", "",
              "Per launch shape (grid = total lanes), from the kernel trace:", "",
-             "| kernel | grid lanes | workgroup | calls | mean us | min us | max us |",
-             "|---|---|---|---|---|---|---|"]
+             "| kernel | grid lanes | workgroup | calls | mean us | median us | min us | max us |",
+             "|---|---|---|---|---|---|---|---|"]
     for (name, grid, wg), v in sorted(shapes.items(), key=lambda kv: -sum(kv[1])):
         lines.append(f"| `{name}` | {grid} | {wg} | {len(v)} | {sum(v) / len(v) / 1e3:.3f} | "
-                     f"{min(v) / 1e3:.3f} | {max(v) / 1e3:.3f} |")
+                     f"{median(v) / 1e3:.3f} | {min(v) / 1e3:.3f} | {max(v) / 1e3:.3f} |")
     if stats:
         lines += ["", "rocprofv3 --stats summary (all kernels of the run, every shape pooled):", "",
                   "| kernel | calls | mean us | share % |", "|---|---|---|---|"]
@@ -462,11 +655,58 @@ def summarize_ktrace(directory: str, out_path: str, command: str):
                 nm = nm[:87] + "..."
             lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                          f"{float(r['Percentage']):.2f} |")
-    lines.append("")
+    # The workload's kernel at its launch shape (grid = min(rows, 65536)
+    # workgroups for the row kernel; the shape with the most calls otherwise).
+    is_kernel = _kernel_filter(workload)
+    mine = [(k, v) for k, v in shapes.items() if is_kernel(k[0])]
+    if not w.sum_only:
+        wgs = min(w.rows, 65536)
+        mine = [(k, v) for k, v in mine if k[1] == wgs * k[2]] or mine
+    if not mine:
+        raise SystemExit(f"no dispatch of the {workload} kernel in the trace")
+    (name, grid, wg), v = max(mine, key=lambda kv: len(kv[1]))
+    lines += ["", f"workload: {workload}", f"kernel_source_hash: {kernel_source_hash()}",
+              f"kernel: {name}", f"launch: {grid // wg} workgroups x {wg} lanes",
+              f"calls: {len(v)}", f"mean_us: {sum(v) / len(v) / 1e3:.3f}",
+              f"median_us: {median(v) / 1e3:.3f}", ""]
     text = "\n".join(lines)
     with open(out_path, "w") as f:
         f.write(text)
     print(text)
+
+
+# ------------------------------------------------------ profile workloads --
+
+def profile_workload(name, torch, arn, dev, steps):
+    """Only the calls of workload `name`, each on bytes that no earlier call
+    touched since the last flush, for rocprofv3 (kernel trace or counters):
+    the prefill step with rotating output sets, the share's ranks in turn,
+    and the small workloads on disjoint windows."""
+    from all_reduce_rmsnorm_amd import synth
+
+    if name == SHARE_WORKLOAD:
+        w = synth.WORKLOADS[DEFAULT_WORKLOAD]
+        d = alloc_workload(w, torch, dev)
+        stg = [torch.empty((arn.arnfp8_stage_bytes(w.rows, w.cols, SHARE_NGPUS),),
+                           dtype=torch.uint8, device=dev) for _ in range(SHARE_NGPUS)]
+        fn = rotating(share_calls(w, d, arn, stg))
+    elif name == DEFAULT_WORKLOAD:
+        w = synth.WORKLOADS[name]
+        fn = step_fn(w, alloc_workload(w, torch, dev, out_sets=out_sets_for(w)), arn)
+    else:
+        w = synth.WORKLOADS[name]
+        wins = alloc_windows(w, torch, dev, max(steps, 8))
+        fn = rotating([call_on(w, d, arn) for d in wins])
+    # The inputs were just written by the generator: flush them out of the
+    # caches, so that every profiled call reads its bytes from HBM.
+    flush = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    flush.fill_(0x5A)
+    torch.cuda.synchronize()
+    del flush
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    log(f"profile workload {name}: {steps} calls")
 
 
 # -------------------------------------------------------------------- main --
@@ -476,25 +716,29 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=None,
                     help="input seed (default: the workload's own, 0)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-latency", action="store_true")
+    ap.add_argument("--no-latency", action="store_true",
+                    help="time the headline step only (no share, formats, latency or references)")
     ap.add_argument("--pmc-calib", action="store_true",
                     help="first run one plain device copy of 1 GiB (scales the HBM counters)")
+    ap.add_argument("--profile-workload", metavar="NAME",
+                    help="run only NAME's calls (--steps of them), for rocprofv3")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="the workload a --summarize-* run describes")
     ap.add_argument("--summarize-pmc", metavar="DIR")
-    ap.add_argument("--pmc-out", default=PMC_SUMMARY)
     ap.add_argument("--summarize-ktrace", metavar="DIR")
-    ap.add_argument("--ktrace-out")
-    ap.add_argument("--ktrace-command", default="")
+    ap.add_argument("--command", default="", help="the profiled command, for the summary")
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, args.pmc_out, args.workload)
+        summarize_pmc(args.summarize_pmc, profile_path(args.workload, "hbm_traffic"),
+                      args.workload, args.command)
         return 0
     if args.summarize_ktrace:
-        summarize_ktrace(args.summarize_ktrace, args.ktrace_out, args.ktrace_command)
+        summarize_ktrace(args.summarize_ktrace, profile_path(args.workload, "kernel_trace"),
+                         args.command, args.workload)
         return 0
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
@@ -522,21 +766,26 @@ def main():
         torch.cuda.synchronize()
         log(f"pmc calibration copy: {src.numel() * 2} bytes read, {dst.numel() * 2} bytes written")
         del src, dst
+    if args.profile_workload:
+        profile_workload(args.profile_workload, torch, arn, dev, args.steps)
+        return 0
 
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[DEFAULT_WORKLOAD]
     log(f"bench: workload {w.name}, steps {args.steps}, warmup {args.warmup}")
     n_out = out_sets_for(w)
     d = alloc_workload(w, torch, dev, out_sets=n_out, seed=args.seed)
     torch.cuda.synchronize()
     fn = step_fn(w, d, arn)
-    ms_per_step, kern_ms = time_steps(torch, fn, args.steps, args.warmup)
+    ms_per_step, kern_ms, seg_ms = time_steps(torch, fn, args.steps, args.warmup, segments=5)
     alg = w.algorithmic_bytes()
     value = alg / (ms_per_step * 1e-3) / 1e9
     achieved = alg / (kern_ms * 1e-3) / 1e9
-    log(f"bench: {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events)")
+    log(f"bench: {ms_per_step * 1e3:.2f} us/step wall, {kern_ms * 1e3:.2f} us/launch (events), "
+        f"segments {[round(x * 1e3, 2) for x in seg_ms]}")
 
     khash = kernel_source_hash()
-    traffic = read_traffic(khash) if w.name == DEFAULT_WORKLOAD else None
+    traffic = read_traffic(khash)
+    k_trace = read_profile(profile_path(w.name, "kernel_trace"), "mean_us", khash)
     result = {
         "metric": "fused sum+RMSNorm+FP8 quant: achieved HBM GB/s (% of peak) and us/call",
         "value": round(value, 2),
@@ -551,7 +800,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "io_dtypes": "bf16 in, bf16 residual out, e4m3fn + f32 scales out" if not w.sum_only else "bf16 in, bf16 out",
+        "io_dtypes": "bf16 in, bf16 residual out, e4m3fn + f32 scales out",
         "data": "synthetic (seeded; inputs resident in HBM)",
         "output_sets": n_out,
         "config": {"workload": w.name, "seed": w.seed if args.seed is None else args.seed,
@@ -562,9 +811,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel_us": round(kern_ms * 1e3, 3),
+                     "kernel_us_median_of_5_segments": round(median(seg_ms) * 1e3, 3),
+                     "kernel_us_segments": [round(x * 1e3, 3) for x in seg_ms],
+                     "kernel_us_trace": k_trace,
                      "kernel_source_hash": khash},
     }
-    if not w.sum_only and not args.no_latency:
+    if not args.no_latency:
         # The unfused chain the fusion removes: the sum is written to HBM as
         # bf16 and read back by a second launch (the fused kernel with P = 1).
         s_bufs = [torch.empty((w.rows, w.cols), dtype=torch.bfloat16, device=dev)
@@ -576,7 +828,7 @@ def main():
                                            o["scales"], d["gamma"], w.eps, w.weight_offset,
                                            w.scale_ub))
         unfused = rotating([unfused_one(o, sb) for o, sb in zip(d["outs"], s_bufs)])
-        un_ms, _ = time_steps(torch, unfused, max(5, args.steps // 2), 3)
+        un_ms, _, _ = time_steps(torch, unfused, max(5, args.steps // 2), 3)
         result["unfused_two_launch"] = {
             "us_per_call": round(un_ms * 1e3, 2),
             "extra_bytes_per_step": 4 * w.numel,
@@ -596,94 +848,77 @@ def main():
         for name, fmt in (("e5m2", arn.FMT_E5M2), ("mxfp8", arn.FMT_MXFP8)):
             scs = mx_scales if fmt == arn.FMT_MXFP8 else [o["scales"] for o in d["outs"]]
             f = rotating([fmt_one(o, sc, fmt) for o, sc in zip(d["outs"], scs)])
-            _, f_k = time_steps(torch, f, max(10, args.steps // 2), 3)
+            _, f_k, _ = time_steps(torch, f, max(10, args.steps // 2), 3)
             fmt_out[f"{name}_us_per_call"] = round(f_k * 1e3, 2)
         result["formats"] = fmt_out
         del mx_scales
         # The residual updated in place (residual_out == residual_in), as a
         # transformer's residual stream is: each output set carries its own
         # residual copy, so the rotation still keeps every call out of cache.
-        if d["residual"] is not None:
-            res_sets = [d["residual"].clone() for _ in d["outs"]]
+        res_sets = [d["residual"].clone() for _ in d["outs"]]
 
-            def in_place_one(o, r):
-                return lambda: arn.arnfp8_run(d["inputs"], r, r, o["out"], o["scales"], d["gamma"],
-                                              w.eps, w.weight_offset, w.scale_ub)
-            _, ip_k = time_steps(torch, rotating([in_place_one(o, r) for o, r in
-                                                  zip(d["outs"], res_sets)]),
-                                 max(10, args.steps // 2), 3)
-            result["in_place_residual"] = {
-                "us_per_call": round(ip_k * 1e3, 2),
-                "gbs": round(alg / (ip_k * 1e-3) / 1e9, 1),
-            }
-            del res_sets
-        # One rank's share of the two-stage layout (8 ranks): the single-GPU
-        # half of the large-payload path, at its real shape.
-        ngpus = 8
-        stg = torch.empty((arn.arnfp8_stage_bytes(w.rows, w.cols, ngpus),), dtype=torch.uint8,
-                          device=dev)
-        share_rows = -(-w.rows // ngpus)
-
-        # The ranks' shares in turn: each call reads other rows and writes
-        # another staging slot, so no call finds its inputs in cache.
-        def share_one(rank):
-            return lambda: arn.arnfp8_run_share(
-                d["inputs"], d["residual"], d["res_out"], stg, d["gamma"], w.eps,
-                w.weight_offset, w.scale_ub, ngpus=ngpus, rank=rank)
-        sh_ms, sh_k = time_steps(torch, rotating([share_one(r) for r in range(ngpus)]),
-                                 max(16, args.steps), 3)
-        share_bytes = (2 * w.P + 4 + 1) * share_rows * w.cols + 4 * share_rows + 2 * w.cols
+        def in_place_one(o, r):
+            return lambda: arn.arnfp8_run(d["inputs"], r, r, o["out"], o["scales"], d["gamma"],
+                                          w.eps, w.weight_offset, w.scale_ub)
+        _, ip_k, _ = time_steps(torch, rotating([in_place_one(o, r) for o, r in
+                                                 zip(d["outs"], res_sets)]),
+                                max(10, args.steps // 2), 3)
+        result["in_place_residual"] = {"us_per_call": round(ip_k * 1e3, 2),
+                                       "gbs": round(alg / (ip_k * 1e-3) / 1e9, 1)}
+        del res_sets
+        # The two-stage share (8 ranks of 1024 rows, the single-GPU half of the
+        # large-payload path at its real shape): the ranks' calls in turn, each
+        # reading other rows and writing its own staging slot (1.2 GB of
+        # inputs per round of 8, so every call runs out of cache).  Replayed
+        # from a graph: eager launches from Python are host-bound at this size.
+        stg = [torch.empty((arn.arnfp8_stage_bytes(w.rows, w.cols, SHARE_NGPUS),),
+                           dtype=torch.uint8, device=dev) for _ in range(SHARE_NGPUS)]
+        calls = share_calls(w, d, arn, stg)
+        sh_graph = graph_us_per_call(torch, calls * 4, reps=7)
+        _, sh_eager, _ = time_steps(torch, rotating(calls), 4 * SHARE_NGPUS, SHARE_NGPUS)
+        sb = share_bytes(w)
+        sh_trace = read_profile(profile_path(SHARE_WORKLOAD, "kernel_trace"), "mean_us", khash)
         result["two_stage_share"] = {
-            "ngpus": ngpus, "rank": "0-7 in turn", "rows": share_rows,
-            "us_per_call": round(sh_k * 1e3, 2),
-            "gbs": round(share_bytes / (sh_k * 1e-3) / 1e9, 1),
+            "ngpus": SHARE_NGPUS, "rank": "0-7 in turn", "rows": -(-w.rows // SHARE_NGPUS),
+            "algorithmic_bytes": sb,
+            "graph_us_per_call": round(sh_graph, 3),
+            "eager_us_per_call": round(sh_eager * 1e3, 3),
+            "roofline": {
+                "bound": "hbm", "achieved": round(sb / (sh_graph * 1e-6) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(sb / (sh_graph * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernel_us_trace": sh_trace,
+                "frac_kernel_trace": (round(sb / (sh_trace * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                      if sh_trace else None),
+                "traffic": read_profile(profile_path(SHARE_WORKLOAD, "hbm_traffic"),
+                                        "traffic_bytes_per_launch", khash)},
         }
-        del stg
-        # Achievable-bandwidth references on the same device: a plain copy
-        # (the P = 1 sum kernel, 1 GiB each way) and the P-slab sum alone.
-        src = torch.ones((65536, 8192), dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        cp_ms, cp_k = time_steps(torch, lambda: arn.arn_sum_bf16([src], dst), 10, 3)
-        del src, dst
-        sm_ms, sm_k = time_steps(torch, rotating([(lambda sb=sb: arn.arn_sum_bf16(d["inputs"], sb))
-                                                  for sb in s_bufs]), 10, 3)
+        log(f"bench: two-stage share {result['two_stage_share']}")
+        del stg, calls
+        result["reference_kernels"] = reference_kernels(w, d, torch, arn, dev, s_bufs)
+        result["reference_kernels"]["fused_kernel_us"] = round(kern_ms * 1e3, 2)
+        log(f"bench: reference kernels {result['reference_kernels']}")
         del s_bufs
-        result["reference_kernels"] = {
-            "copy_1GiB_gbs": round(2 * (1 << 30) / (cp_k * 1e-3) / 1e9, 1),
-            "sum_only_same_slabs_gbs": round((2 * w.P + 2) * w.numel / (sm_k * 1e-3) / 1e9, 1),
-        }
+        torch.cuda.empty_cache()
     props = torch.cuda.get_device_properties(dev)
     result["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                         "compute_units": props.multi_processor_count,
                         "hbm_gib": round(props.total_memory / 2**30, 1)}
     if not args.no_latency:
+        flush = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
         lat = {}
-        for name in DECODE_WORKLOADS:
-            wd = synth.WORKLOADS[name]
-            dd = alloc_workload(wd, torch, dev)
-            lat[name] = round(graph_us_per_call(torch, step_fn(wd, dd, arn)), 3)
-            del dd
-        result["latency_us_per_call"] = lat
-        log(f"bench: graph-replayed latency {lat}")
-        cold = {}
-        for name in DECODE_WORKLOADS:
-            us, nsets = graph_us_per_call_cold(torch, synth.WORKLOADS[name], arn, dev)
-            if us is not None:
-                cold[name] = round(us, 3)
-        result["latency_us_per_call_cold"] = cold
-        log(f"bench: graph-replayed latency, inputs not in cache {cold}")
-        # The same figures as algorithmic bytes per second (latency-bound
-        # shapes: these are far below the HBM peak by nature).
-        result["latency_gbs"] = {
-            kind: {n: round(synth.WORKLOADS[n].algorithmic_bytes() / (us * 1e-6) / 1e9, 1)
-                   for n, us in table.items()}
-            for kind, table in (("warm", lat), ("cold", cold))}
+        for name in LATENCY_WORKLOADS:
+            lat[name] = latency_figures(synth.WORKLOADS[name], torch, arn, dev, flush, khash)
+            log(f"bench: latency {name} {lat[name]}")
+        result["latency"] = lat
+        del flush
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, d, torch)
         log(f"bench: cpu baseline {result['cpu_baseline']}")
         result["cpu_oracle_threaded"] = cpu_oracle_threaded(w, d, torch)
         log(f"bench: oracle on a thread pool {result['cpu_oracle_threaded']}")
-        result["cpu_oracle_us_per_call"] = cpu_oracle_latency(DECODE_WORKLOADS)
+        result["cpu_oracle_us_per_call"] = cpu_oracle_latency(LATENCY_WORKLOADS)
         log(f"bench: oracle per call on the small workloads {result['cpu_oracle_us_per_call']}")
     print(json.dumps(result), flush=True)
     return 0
