@@ -116,6 +116,9 @@ __device__ __forceinline__ void store16(u32x4 *p, u32x4 v) { __builtin_nontempor
 // (~197 us) only when the same output buffers are rewritten while they are
 // still cache-resident.  For decode batches nt is also the fastest (P = 4
 // [32, 7168], inputs not in cache: 4.9 us nt, 5.2 us default policy).
+// s_waitcnt operand (gfx9 encoding) that waits for vmcnt == 0 only: expcnt
+// and lgkmcnt at their maxima (7 in bits 6:4, 15 in bits 11:8), vmcnt 0.
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kStoreNt = 2;    // cache-policy operand bit of nt
 constexpr int kStoreSc1 = 16;  // cache-policy operand bit of sc1
 // Word 3 of a raw (untyped, unswizzled, stride-0) buffer resource on
@@ -363,6 +366,7 @@ template <int FMT, int P, int VPT, bool RES_IN, bool RES_OUT, bool SC1>
 __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowArgs a) {
   constexpr int G = load_group<P, VPT, RES_IN>();
   constexpr bool KEEP_HG = VPT <= 8;
+  constexpr bool DEFER_STORES = P <= 4;  // residual stores after the group's loads
   __shared__ float red[2][16][2];  // [row parity][wave][sum h^2, max |h g|]
   const int t = threadIdx.x;
   const int T = blockDim.x;
@@ -406,15 +410,17 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
         g[k] = a.gamma[c];
       }
       if (v0 == 0) __builtin_amdgcn_s_setprio(3);
+      u32x4 hs[G];
 #pragma unroll
       for (int k = 0; k < G; ++k) {
         const int v = v0 + k;
         const bool valid = v * T + t <= last;
         u32x4 hv = rank_order_sum<P>(x[k]);
         if constexpr (RES_IN) hv = add_bf16(hv, r[k]);
-        if constexpr (RES_OUT) {
+        if constexpr (RES_OUT && !DEFER_STORES) {
           if (valid) buf_store16<SC1>(rout, (v * T + t) * 16, hv);
         }
+        hs[k] = hv;
         if constexpr (!KEEP_HG) hk[v] = hv;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -430,6 +436,26 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
             ss += h1 * h1;
             mx = fmaxf(mx, fmaxf(fabsf(y0), fabsf(y1)));
           }
+        }
+      }
+      // With up to four slabs (DEFER_STORES) the group's residual stores go
+      // out only once every load of the group has arrived.  A store issued while loads are
+      // still pending leaves reads and writes mixed in the one vector-memory
+      // counter, and a later wait for a load (the gamma loads come last) then
+      // waits for the store as well, which puts the store's completion on the
+      // row's critical path ahead of the reduction.  The explicit wait is for
+      // loads only (no store is pending yet).  Measured on MI355X, 512 x 2
+      // lanes, inputs out of cache: P = 4 over 7168 columns 4.97 against
+      // 5.11 us at 1 row, 5.47 / 5.58 at 32, 6.2 / 6.4 at 128, level from 512
+      // rows; with eight slabs the early store is better (P = 8: 5.92 against
+      // 6.03 us at 1 row; 204.8 against 206.7 us at 8192 rows), as waiting
+      // for twenty loads delays the first store more than the late wait costs.
+      if constexpr (RES_OUT && DEFER_STORES) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          const int v = v0 + k;
+          if (v * T + t <= last) buf_store16<SC1>(rout, (v * T + t) * 16, hs[k]);
         }
       }
       // Keep the next group's loads below this point: hoisting them would

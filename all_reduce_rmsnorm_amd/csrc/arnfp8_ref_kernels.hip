@@ -15,8 +15,10 @@
 //                 updated residual and the fp8 row), each the XOR of the
 //                 chunk's loads (so every store waits for its loads, as in
 //                 the fused kernel), no other arithmetic.
+//   arnref_empty  a kernel that does nothing, on the grid of one workgroup per
+//                 row: the cost of a launch alone.
 // Shapes follow the fused kernel: lanes = T, chunks per lane = V, T * V * 16
-// >= row_bytes.
+// >= row_bytes; up to 1024 lanes with one chunk per lane, else up to 512.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,7 +43,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int byt
 }
 
 template <int S, int V>
-__global__ __launch_bounds__(512) void read_kernel(Streams in, u32x4 *__restrict__ sink,
+__global__ __launch_bounds__(V == 1 ? 1024 : 512) void read_kernel(Streams in, u32x4 *__restrict__ sink,
                                                    int64_t rows, int c16) {
   const int t = threadIdx.x, T = blockDim.x, last = c16 - 1;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(512) void read_kernel(Streams in, u32x4 *__restrict
 }
 
 template <int W, int V>
-__global__ __launch_bounds__(512) void write_kernel(OutStreams out, int64_t rows, int c16) {
+__global__ __launch_bounds__(V == 1 ? 1024 : 512) void write_kernel(OutStreams out, int64_t rows, int c16) {
   const int t = threadIdx.x, T = blockDim.x, last = c16 - 1;
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const int64_t base = row * (int64_t)c16;
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(512) void write_kernel(OutStreams out, int64_t rows
 }
 
 template <int S, int V>
-__global__ __launch_bounds__(512) void twin_kernel(Streams in, u32x4 *__restrict__ out16,
+__global__ __launch_bounds__(V == 1 ? 1024 : 512) void twin_kernel(Streams in, u32x4 *__restrict__ out16,
                                                    u32x2 *__restrict__ out8, int64_t rows,
                                                    int c16) {
   const int t = threadIdx.x, T = blockDim.x, last = c16 - 1;
@@ -114,6 +116,8 @@ __global__ __launch_bounds__(512) void twin_kernel(Streams in, u32x4 *__restrict
     }
   }
 }
+
+__global__ __launch_bounds__(1024) void empty_kernel(int64_t rows) {}
 
 typedef void (*ReadK)(Streams, u32x4 *, int64_t, int);
 typedef void (*WriteK)(OutStreams, int64_t, int);
@@ -162,7 +166,7 @@ TwinK twin_table(int s, int v) {
 bool shape(int c16, int *threads, int *vpt) {
   if (*vpt == 0) *vpt = c16 <= 512 ? 1 : (c16 <= 1024 ? 2 : 4);
   if (*threads == 0) *threads = ((c16 + *vpt - 1) / *vpt + 63) / 64 * 64;
-  return *threads >= 64 && *threads <= 512 && *threads % 64 == 0 &&
+  return *threads >= 64 && *threads <= (*vpt == 1 ? 1024 : 512) && *threads % 64 == 0 &&
          (int64_t)*threads * *vpt >= c16;
 }
 
@@ -219,4 +223,9 @@ extern "C" int arnref_twin(const void *const *streams, int nstreams, void *out16
   Streams s;
   for (int i = 0; i < kMaxStreams; ++i) s.p[i] = (const u32x4 *)streams[i < nstreams ? i : 0];
   return launch(k, rows, threads, stream, s, (u32x4 *)out16, (u32x2 *)out8, rows, c16);
+}
+
+extern "C" int arnref_empty(int64_t rows, int threads, hipStream_t stream) {
+  if (rows <= 0 || threads < 64 || threads > 1024 || threads % 64) return 3;
+  return launch(empty_kernel, rows, threads, stream, rows);
 }

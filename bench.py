@@ -353,7 +353,8 @@ def ref_library():
         L.arnref_read.argtypes = [ctypes.POINTER(vp), ci, vp, i64, i64, ci, ci, vp]
         L.arnref_write.argtypes = [ctypes.POINTER(vp), ci, i64, i64, ci, ci, vp]
         L.arnref_twin.argtypes = [ctypes.POINTER(vp), ci, vp, vp, i64, i64, ci, ci, vp]
-        for f in (L.arnref_read, L.arnref_write, L.arnref_twin):
+        L.arnref_empty.argtypes = [i64, ci, vp]
+        for f in (L.arnref_read, L.arnref_write, L.arnref_twin, L.arnref_empty):
             f.restype = ci
         _ref = L
     return _ref
@@ -409,6 +410,77 @@ def reference_kernels(w, d, torch, arn, dev, s_bufs, steps=20):
     out["note"] = ("read/write kernels of libarnfp8_ref.so: one workgroup per row, 16-byte "
                    "non-temporal loads and stores, no arithmetic; twin = the fused kernel's "
                    "byte mix (9 read streams, 16 + 8 bytes written per chunk)")
+    return out
+
+
+# The launch shape the library picks for these workloads (one chunk per lane
+# for eight slabs up to one row per CU, else 512 lanes of two chunks), used by
+# every kernel of the breakdown below.
+BREAKDOWN = {"decode_p4_32x7168": (512, 2), "unit_offset_p8_128x8192": (1024, 1)}
+
+
+def decode_breakdown(w, torch, arn, dev, flush, nwin=64):
+    """Where a small workload's time goes: graph-replayed microseconds per
+    call (cold: every call on its own inputs after a 1 GiB flush; warm: the
+    same inputs every call) of kernels on the same grid that do successively
+    more of the fused kernel's work: nothing (the launch), the loads of the
+    slabs and residual, the loads and the stores (the traffic twin), and the
+    fused kernel itself (adds the row reduction and the row scalars)."""
+    import ctypes
+
+    L = ref_library()
+    threads, vpt = BREAKDOWN[w.name]
+    wins = alloc_windows(w, torch, dev, nwin)
+    sink = torch.empty((w.rows, 16), dtype=torch.uint8, device=dev)
+    # The twin writes its bytes into buffers of its own (never the inputs).
+    tw16 = torch.empty((nwin * w.rows, w.cols), dtype=torch.bfloat16, device=dev)
+    tw8 = torch.empty((nwin * w.rows, w.cols), dtype=torch.uint8, device=dev)
+    arrs = [(ctypes.c_void_p * (w.P + 1))(*[t.data_ptr() for t in d["inputs"] + [d["residual"]]])
+            for d in wins]
+    cur = lambda: torch.cuda.current_stream().cuda_stream
+    launch = {"threads": threads, "vpt": vpt}
+
+    def checked(st):
+        if st != 0:
+            raise RuntimeError(f"reference kernel launch failed with status {st}")
+
+    kinds = {
+        "empty": lambda k: (lambda: checked(L.arnref_empty(w.rows, threads, cur()))),
+        "loads": lambda k: (lambda: checked(L.arnref_read(arrs[k], w.P + 1, sink.data_ptr(), w.rows,
+                                                          2 * w.cols, threads, vpt, cur()))),
+        "loads_and_stores": lambda k: (lambda: checked(L.arnref_twin(
+            arrs[k], w.P + 1, tw16[k * w.rows].data_ptr(), tw8[k * w.rows].data_ptr(), w.rows,
+            2 * w.cols, threads, vpt, cur()))),
+        "fused": lambda k: call_on(w, wins[k], arn, launch=launch),
+    }
+    out = {"launch": f"{w.rows} workgroups x {threads} lanes, {vpt} chunk(s) per lane"}
+    for name, mk in kinds.items():
+        fs = [mk(k) for k in range(nwin)]
+        out[name] = {"warm_us_per_call": round(graph_us_per_call(torch, [fs[0]] * 100), 3),
+                     "cold_us_per_call": round(graph_us_per_call(torch, fs, flush=flush), 3)}
+    del wins, arrs, tw16, tw8
+    torch.cuda.empty_cache()
+    return out
+
+
+def latency_scaling(torch, arn, dev, flush, rows_list=(1, 8, 32, 64, 128, 256, 512, 1024)):
+    """Graph-replayed microseconds per call (cold) of the unit-offset
+    workload's laws (P = 8, 8192 columns) at growing row counts: a fixed
+    latency plus a bandwidth term."""
+    import dataclasses
+
+    from all_reduce_rmsnorm_amd import synth
+
+    base = synth.WORKLOADS["unit_offset_p8_128x8192"]
+    out = {}
+    for r in rows_list:
+        w = dataclasses.replace(base, name=f"unit_offset_p8_{r}x8192", rows=r)
+        wins = alloc_windows(w, torch, dev, min(64, max(8, 8192 // r)))
+        us = graph_us_per_call(torch, [call_on(w, d, arn) for d in wins], flush=flush)
+        out[str(r)] = {"cold_us_per_call": round(us, 3),
+                       "gbs": round(w.algorithmic_bytes() / (us * 1e-6) / 1e9, 1)}
+        del wins
+        torch.cuda.empty_cache()
     return out
 
 
@@ -540,8 +612,9 @@ def _kernel_filter(workload):
 
 
 def summarize_pmc(directory: str, out_path: str, workload: str, command: str = ""):
-    """Build the counter summary from rocprofv3 --pmc CSV output under `directory`:
-    one run with FETCH_SIZE, one with WRITE_SIZE, each holding the workload's
+    """Build the counter summary from rocprofv3 --pmc CSV output under
+    `directory` (or under each of a comma-separated list of directories): one
+    run with FETCH_SIZE, one with WRITE_SIZE, each holding the workload's
     kernel dispatches and one plain copy of known size (``--pmc-calib``)."""
     import csv
 
@@ -550,7 +623,9 @@ def summarize_pmc(directory: str, out_path: str, workload: str, command: str = "
     w = synth.WORKLOADS[workload]
     is_kernel = _kernel_filter(workload)
     per = {}  # counter -> {"kernel": [kib...], "copy": [kib...]}
-    files = sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True))
+    dirs = directory.split(",")
+    files = sorted(f for d in dirs for f in
+                   glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
     if not files:
         raise SystemExit(f"no counter_collection.csv under {directory}")
     for f in files:
@@ -577,19 +652,22 @@ def summarize_pmc(directory: str, out_path: str, workload: str, command: str = "
         total += scaled
         lines.append(f"| {ctr} | {k_kib:.1f} KiB ({len(k)} dispatches) | {c_kib:.0f} KiB | "
                      f"{factor:.4f} | {scaled / 1e6:.3f} MB |")
-    alg = share_bytes(w) if workload == SHARE_WORKLOAD else w.algorithmic_bytes()
+    alg = w.algorithmic_bytes()
     if not command:
         command = (f"python -u bench.py --profile-workload {workload} --pmc-calib")
+    fetch_dir, write_dir = (dirs + dirs)[:2] if len(dirs) > 1 else (f"{directory}/pmc_fetch",
+                                                                  f"{directory}/pmc_write")
     text = "\n".join([
         f"# HBM traffic of `{kernel_name_of(workload)}` on {workload}",
         "",
         "Counters from two `rocprofv3 --pmc` runs (FETCH_SIZE, then WRITE_SIZE), per",
         "dispatch, scaled by what the same counter reads for a plain copy of",
         f"{calib_bytes} bytes (read {calib_bytes} B, write {calib_bytes} B): the P = 1 sum kernel.",
-        "Commands (from the repository root, on one MI355X):",
+        "Every profiled dispatch reads inputs that no earlier dispatch touched since a",
+        "1 GiB cache flush.  Commands (from the repository root, on one MI355X):",
         "",
-        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {directory}/pmc_fetch -o fetch -- {command}",
-        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {directory}/pmc_write -o write -- {command}",
+        f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o fetch -- {command}",
+        f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o write -- {command}",
         f"    python bench.py --summarize-pmc {directory} --workload {workload}",
         "",
         "| counter | kernel (mean per dispatch) | copy kernel | scale factor | scaled bytes |",
@@ -685,11 +763,16 @@ def profile_workload(name, torch, arn, dev, steps):
     from all_reduce_rmsnorm_amd import synth
 
     if name == SHARE_WORKLOAD:
+        # As the benchmark times it: the 8 ranks' calls in turn, four rounds
+        # captured in one graph, replayed `steps` times.
         w = synth.WORKLOADS[DEFAULT_WORKLOAD]
         d = alloc_workload(w, torch, dev)
         stg = [torch.empty((arn.arnfp8_stage_bytes(w.rows, w.cols, SHARE_NGPUS),),
                            dtype=torch.uint8, device=dev) for _ in range(SHARE_NGPUS)]
-        fn = rotating(share_calls(w, d, arn, stg))
+        us = graph_us_per_call(torch, share_calls(w, d, arn, stg) * 4, reps=steps)
+        log(f"profile workload {name}: {steps} graph replays of {4 * SHARE_NGPUS} calls, "
+            f"{us:.3f} us per call")
+        return
     elif name == DEFAULT_WORKLOAD:
         w = synth.WORKLOADS[name]
         fn = step_fn(w, alloc_workload(w, torch, dev, out_sets=out_sets_for(w)), arn)
@@ -911,6 +994,11 @@ def main():
             lat[name] = latency_figures(synth.WORKLOADS[name], torch, arn, dev, flush, khash)
             log(f"bench: latency {name} {lat[name]}")
         result["latency"] = lat
+        result["decode_breakdown"] = {n: decode_breakdown(synth.WORKLOADS[n], torch, arn, dev, flush)
+                                      for n in BREAKDOWN}
+        log(f"bench: decode breakdown {result['decode_breakdown']}")
+        result["latency_scaling_unit_offset_laws"] = latency_scaling(torch, arn, dev, flush)
+        log(f"bench: latency scaling {result['latency_scaling_unit_offset_laws']}")
         del flush
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
