@@ -448,7 +448,7 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
       // lanes, inputs out of cache: P = 4 over 7168 columns 4.97 against
       // 5.11 us at 1 row, 5.47 / 5.58 at 32, 6.2 / 6.4 at 128, level from 512
       // rows; with eight slabs the early store is better (P = 8: 5.92 against
-      // 6.03 us at 1 row; 204.8 against 206.7 us at 8192 rows), as waiting
+      // 6.03 us at 1 row; 205.3 against 206.7 us at 8192 rows), as waiting
       // for twenty loads delays the first store more than the late wait costs.
       if constexpr (RES_OUT && DEFER_STORES) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

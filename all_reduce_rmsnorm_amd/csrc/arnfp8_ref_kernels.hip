@@ -17,6 +17,16 @@
 //                 the fused kernel), no other arithmetic.
 //   arnref_empty  a kernel that does nothing, on the grid of one workgroup per
 //                 row: the cost of a launch alone.
+//   arnref_exchange  the cost of one exchange between workgroups: groups of S
+//                 workgroups each publish one 64-bit word (a 32-bit payload and
+//                 a 32-bit count) with a relaxed device-scope atomic store and
+//                 wait until every partner's word carries the same count, as a
+//                 row split across S workgroups would trade its row statistics.
+//                 Each word has a single writer whose count goes up by one per
+//                 launch, so partners stay in step across launches and graph
+//                 replays with no host-side epoch.  The wait is bounded
+//                 (kSpinLimit polls); a wait that runs out is counted in
+//                 `timeouts` and the workgroup goes on, so every launch ends.
 // Shapes follow the fused kernel: lanes = T, chunks per lane = V, T * V * 16
 // >= row_bytes; up to 1024 lanes with one chunk per lane, else up to 512.
 #include <hip/hip_runtime.h>
@@ -118,6 +128,47 @@ __global__ __launch_bounds__(V == 1 ? 1024 : 512) void twin_kernel(Streams in, u
 }
 
 __global__ __launch_bounds__(1024) void empty_kernel(int64_t rows) {}
+
+constexpr int kSpinLimit = 1 << 16;
+
+// Workgroup b belongs to group b / S (consecutive ids) or, with `stride` 8,
+// to the group of ids that agree modulo 8 (workgroups are dispatched to the
+// eight XCDs in turn, so such a group shares one XCD and its L2).
+__global__ __launch_bounds__(64) void exchange_kernel(unsigned long long *words, int S, int stride,
+                                                      unsigned *timeouts) {
+  const int b = blockIdx.x;
+  int first, step;
+  if (stride == 8) {
+    const int lane8 = b % 8, k = b / 8;  // k-th workgroup on its XCD
+    first = (k / S) * S * 8 + lane8;
+    step = 8;
+  } else {
+    first = (b / S) * S;
+    step = 1;
+  }
+  if (threadIdx.x == 0) {
+    unsigned long long *mine = words + b;
+    const unsigned long long old =
+        __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned count = (unsigned)(old >> 32) + 1u;
+    const unsigned long long word = ((unsigned long long)count << 32) | (unsigned)b;
+    __hip_atomic_store(mine, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool late = false;
+    for (int j = 0; j < S; ++j) {
+      unsigned long long *theirs = words + first + j * step;
+      if (theirs == mine) continue;
+      int spins = 0;
+      while ((unsigned)(__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >>
+                        32) != count) {
+        if (++spins == kSpinLimit) {
+          late = true;
+          break;
+        }
+      }
+    }
+    if (late) atomicAdd(timeouts, 1u);
+  }
+}
 
 typedef void (*ReadK)(Streams, u32x4 *, int64_t, int);
 typedef void (*WriteK)(OutStreams, int64_t, int);
@@ -228,4 +279,22 @@ extern "C" int arnref_twin(const void *const *streams, int nstreams, void *out16
 extern "C" int arnref_empty(int64_t rows, int threads, hipStream_t stream) {
   if (rows <= 0 || threads < 64 || threads > 1024 || threads % 64) return 3;
   return launch(empty_kernel, rows, threads, stream, rows);
+}
+
+// words: nwg zero-initialised 64-bit words, untouched by anything else;
+// timeouts: one 32-bit counter.  nwg must be a multiple of S (and of 8 * S
+// with stride 8); every workgroup of the grid must be resident at once (the
+// bench launches at most one 64-lane workgroup per CU).
+extern "C" int arnref_exchange(void *words, int nwg, int S, int stride, void *timeouts,
+                               hipStream_t stream) {
+  if (words == nullptr || timeouts == nullptr || S < 1 || S > 64 || nwg < S || nwg > 4096 ||
+      (stride != 1 && stride != 8) || nwg % (S * (stride == 8 ? 8 : 1)) != 0)
+    return 3;
+  unsigned long long *w = (unsigned long long *)words;
+  unsigned *t = (unsigned *)timeouts;
+  void *argv[] = {&w, &S, &stride, &t};
+  return hipLaunchKernel((const void *)exchange_kernel, dim3((unsigned)nwg), dim3(64), argv, 0,
+                         stream) == hipSuccess
+             ? 0
+             : 6;
 }

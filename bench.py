@@ -354,7 +354,9 @@ def ref_library():
         L.arnref_write.argtypes = [ctypes.POINTER(vp), ci, i64, i64, ci, ci, vp]
         L.arnref_twin.argtypes = [ctypes.POINTER(vp), ci, vp, vp, i64, i64, ci, ci, vp]
         L.arnref_empty.argtypes = [i64, ci, vp]
-        for f in (L.arnref_read, L.arnref_write, L.arnref_twin, L.arnref_empty):
+        L.arnref_exchange.argtypes = [vp, ci, ci, ci, vp, vp]
+        for f in (L.arnref_read, L.arnref_write, L.arnref_twin, L.arnref_empty,
+                  L.arnref_exchange):
             f.restype = ci
         _ref = L
     return _ref
@@ -416,7 +418,8 @@ def reference_kernels(w, d, torch, arn, dev, s_bufs, steps=20):
 # The launch shape the library picks for these workloads (one chunk per lane
 # for eight slabs up to one row per CU, else 512 lanes of two chunks), used by
 # every kernel of the breakdown below.
-BREAKDOWN = {"decode_p4_32x7168": (512, 2), "unit_offset_p8_128x8192": (1024, 1)}
+BREAKDOWN = {"decode_p4_32x7168": (512, 2), "unit_offset_p8_128x8192": (1024, 1),
+             "token_p8_1x8192": (1024, 1)}
 
 
 def decode_breakdown(w, torch, arn, dev, flush, nwin=64):
@@ -431,7 +434,7 @@ def decode_breakdown(w, torch, arn, dev, flush, nwin=64):
     L = ref_library()
     threads, vpt = BREAKDOWN[w.name]
     wins = alloc_windows(w, torch, dev, nwin)
-    sink = torch.empty((w.rows, 16), dtype=torch.uint8, device=dev)
+    sink = torch.empty((8 * w.rows, 16), dtype=torch.uint8, device=dev)
     # The twin writes its bytes into buffers of its own (never the inputs).
     tw16 = torch.empty((nwin * w.rows, w.cols), dtype=torch.bfloat16, device=dev)
     tw8 = torch.empty((nwin * w.rows, w.cols), dtype=torch.uint8, device=dev)
@@ -453,6 +456,21 @@ def decode_breakdown(w, torch, arn, dev, flush, nwin=64):
             2 * w.cols, threads, vpt, cur()))),
         "fused": lambda k: call_on(w, wins[k], arn, launch=launch),
     }
+    # The same bytes spread over `parts` times as many workgroups, each
+    # reading (and writing) 1/parts of a row: what splitting rows across
+    # workgroups could save on the memory side, before the cost of exchanging
+    # the row statistics between them.
+    parts = max(1, min(8, 256 // w.rows))
+    if parts > 1 and (w.cols // 8) % parts == 0:
+        sub_c16 = w.cols // 8 // parts
+        sub_threads = max(64, -(-sub_c16 // 64) * 64)
+        kinds[f"loads_over_{parts * w.rows}_workgroups"] = lambda k: (lambda: checked(L.arnref_read(
+            arrs[k], w.P + 1, sink.data_ptr(), parts * w.rows, 16 * sub_c16, sub_threads, 1,
+            cur())))
+        kinds[f"loads_and_stores_over_{parts * w.rows}_workgroups"] = lambda k: (
+            lambda: checked(L.arnref_twin(arrs[k], w.P + 1, tw16[k * w.rows].data_ptr(),
+                                          tw8[k * w.rows].data_ptr(), parts * w.rows,
+                                          16 * sub_c16, sub_threads, 1, cur())))
     out = {"launch": f"{w.rows} workgroups x {threads} lanes, {vpt} chunk(s) per lane"}
     for name, mk in kinds.items():
         fs = [mk(k) for k in range(nwin)]
@@ -460,6 +478,33 @@ def decode_breakdown(w, torch, arn, dev, flush, nwin=64):
                      "cold_us_per_call": round(graph_us_per_call(torch, fs, flush=flush), 3)}
     del wins, arrs, tw16, tw8
     torch.cuda.empty_cache()
+    return out
+
+
+def exchange_cost(torch, dev, nwg=256, calls=64):
+    """Graph-replayed microseconds per launch of 256 one-wave workgroups that
+    do nothing, and of the same grid exchanging one 64-bit word within groups
+    of 2 and 8 workgroups (consecutive ids, or ids equal modulo 8, which
+    share an XCD): the price of the cross-workgroup step a split row needs."""
+    L = ref_library()
+    cur = lambda: torch.cuda.current_stream().cuda_stream
+    words = torch.zeros((nwg,), dtype=torch.int64, device=dev)
+    timeouts = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def checked(st):
+        if st != 0:
+            raise RuntimeError(f"reference kernel launch failed with status {st}")
+
+    out = {"workgroups": nwg, "empty_us_per_call": round(graph_us_per_call(
+        torch, [lambda: checked(L.arnref_empty(nwg, 64, cur()))] * calls), 3)}
+    for S in (2, 8):
+        for stride, where in ((1, "consecutive"), (8, "same_xcd")):
+            f = lambda S=S, stride=stride: checked(L.arnref_exchange(
+                words.data_ptr(), nwg, S, stride, timeouts.data_ptr(), cur()))
+            out[f"groups_of_{S}_{where}_us_per_call"] = round(graph_us_per_call(
+                torch, [f] * calls), 3)
+    torch.cuda.synchronize()
+    out["timeouts"] = int(timeouts.item())
     return out
 
 
@@ -824,7 +869,7 @@ def main():
                          args.command, args.workload)
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU exchange is out of scope; run with --gpus 1)", file=sys.stderr)
         return 2
 
@@ -997,6 +1042,8 @@ def main():
         result["decode_breakdown"] = {n: decode_breakdown(synth.WORKLOADS[n], torch, arn, dev, flush)
                                       for n in BREAKDOWN}
         log(f"bench: decode breakdown {result['decode_breakdown']}")
+        result["exchange_cost"] = exchange_cost(torch, dev)
+        log(f"bench: exchange cost {result['exchange_cost']}")
         result["latency_scaling_unit_offset_laws"] = latency_scaling(torch, arn, dev, flush)
         log(f"bench: latency scaling {result['latency_scaling_unit_offset_laws']}")
         del flush
