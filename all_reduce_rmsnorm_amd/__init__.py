@@ -22,6 +22,7 @@ __all__ = [
     "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW", "arnfp8_stage_bytes",
     "arnfp8_run_share", "SIMD_WIDTH", "arnfp8_run_fmt", "FMT_E4M3FN", "FMT_E5M2", "FMT_MXFP8",
     "CVT_BF16", "arnfp8_convert_f32", "STORES_AUTO", "STORES_NT", "STORES_SC1",
+    "SplitOpts", "arnfp8_split_workspace_bytes", "arnfp8_run_split",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +34,7 @@ STATUS = {
     0: "ARNFP8_OK", 1: "ARNFP8_NULL_POINTER", 2: "ARNFP8_MISALIGNED", 3: "ARNFP8_BAD_SHAPE",
     4: "ARNFP8_BAD_P", 5: "ARNFP8_ALIAS", 6: "ARNFP8_HIP_ERROR", 7: "ARNFP8_BAD_CONFIG",
     8: "ARNFP8_BAD_SHARE", 9: "ARNFP8_BAD_FORMAT", 10: "ARNFP8_BAD_SCALAR",
+    11: "ARNFP8_BAD_WORKSPACE",
 }
 FMT_E4M3FN = 0
 FMT_E5M2 = 1
@@ -63,6 +65,13 @@ class Launch(ctypes.Structure):
 STORES_AUTO = 0
 STORES_NT = 1
 STORES_SC1 = 2
+
+
+class SplitOpts(ctypes.Structure):
+    """``arnfp8_split_opts``: parts per row (0: automatic) and the bound of the
+    wait for a partner's partial (0: default; -1: none, the fallback alone)."""
+
+    _fields_ = [("parts", ctypes.c_int), ("spin_polls", ctypes.c_int)]
 
 
 _lib = None
@@ -101,6 +110,12 @@ def library() -> ctypes.CDLL:
         L.arnfp8_run_share.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, vp]
+        L.arnfp8_split_workspace_bytes.restype = ctypes.c_int64
+        L.arnfp8_split_workspace_bytes.argtypes = [i64]
+        L.arnfp8_run_split.restype = ctypes.c_int
+        L.arnfp8_run_split.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int,
+                                       vp, i64, vp, ctypes.POINTER(SplitOpts)]
         L.arn_sum_bf16.restype = ctypes.c_int
         L.arn_sum_bf16.argtypes = [ctypes.POINTER(vp), vp, i64, i64, ctypes.c_int, vp]
         L.arnfp8_status_string.restype = ctypes.c_char_p
@@ -280,6 +295,39 @@ def arnfp8_run_fmt(inputs, residual_in, residual_out, out_fp8, scales, gamma, ep
                                   cols, P, int(out_format), _stream(stream), opt)
     if st != 0:
         raise ArnFp8Error("arnfp8_run_fmt", st)
+
+
+def arnfp8_split_workspace_bytes(rows: int) -> int:
+    """Bytes of the workspace ``arnfp8_run_split`` needs for ``rows`` rows (-1 if invalid)."""
+    return int(library().arnfp8_split_workspace_bytes(int(rows)))
+
+
+def arnfp8_run_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                     weight_offset, scale_ub, rows=None, cols=None, P=None, workspace=None,
+                     workspace_bytes=None, stream=None, opts=None) -> None:
+    """The fused epilogue (e4m3fn) with each row split across several
+    workgroups that trade their row statistics through ``workspace`` (a device
+    tensor of at least ``arnfp8_split_workspace_bytes(rows)`` bytes, zeroed
+    before its first use and then reused as is).  ``opts``: a ``SplitOpts``,
+    a dict of its fields, or None.  The residual cannot be updated in place."""
+    rows, cols, P = _shape(inputs, rows, cols, P)
+    if isinstance(opts, dict):
+        opts = SplitOpts(**opts)
+    opt = ctypes.byref(opts) if opts is not None else None
+    n = rows * cols
+    if workspace_bytes is None:
+        workspace_bytes = (workspace.numel() * workspace.element_size()
+                           if workspace is not None and not isinstance(workspace, int) else 0)
+    ptrs = (_ptr_array(inputs, 2 * n), _ptr(residual_in, _BF16, "residual_in", 2 * n),
+            _ptr(residual_out, _BF16, "residual_out", 2 * n), _ptr(out_fp8, _FP8, "out_fp8", n),
+            _ptr(scales, _F32, "scales", 4 * rows), _ptr(gamma, _BF16, "gamma", 2 * cols))
+    ws = _ptr(workspace, None, "workspace", None)
+    _on_device(inputs=inputs, residual_in=residual_in, residual_out=residual_out,
+               out_fp8=out_fp8, scales=scales, gamma=gamma, workspace=workspace)
+    st = library().arnfp8_run_split(*ptrs, float(eps), float(weight_offset), float(scale_ub),
+                                    rows, cols, P, ws, int(workspace_bytes), _stream(stream), opt)
+    if st != 0:
+        raise ArnFp8Error("arnfp8_run_split", st)
 
 
 def arnfp8_convert_f32(inp, out, fmt, n=None, stream=None) -> None:

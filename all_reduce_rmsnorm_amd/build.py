@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 # device code lives in csrc/arnfp8_kernels.hpp; each arnfp8_rows_*.hip holds
 # one output format's kernel instances.
 SOURCES = [os.path.join(PKG, "csrc", f) for f in
-           ("arnfp8.hip", "arnfp8_rows_e4m3.hip", "arnfp8_rows_e5m2.hip", "arnfp8_rows_mxfp8.hip")]
+           ("arnfp8.hip", "arnfp8_rows_e4m3.hip", "arnfp8_rows_e5m2.hip", "arnfp8_rows_mxfp8.hip",
+            "arnfp8_split.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libarnfp8.so")
 # Achievable-bandwidth reference kernels for the benchmark, in a library of

@@ -402,6 +402,91 @@ extern "C" int arnfp8_run_share(const void *const *inputs, const void *residual_
                 dim3(cfg.grid), dim3(cfg.threads), stream, a);
 }
 
+extern "C" int64_t arnfp8_split_workspace_bytes(int64_t rows) {
+  if (rows < 0 || rows > INT64_MAX / (16 * kSplitSlots)) return -1;
+  return rows * 2 * kSplitSlots * (int64_t)sizeof(unsigned long long);
+}
+
+extern "C" int arnfp8_run_split(const void *const *inputs, const void *residual_in,
+                                void *residual_out, void *out_fp8, float *scales,
+                                const void *gamma, float eps, float weight_offset, float scale_ub,
+                                int64_t rows, int64_t cols, int P, void *workspace,
+                                int64_t workspace_bytes, hipStream_t stream,
+                                const arnfp8_split_opts *opt) {
+  int st = check_shape(rows, cols, P);
+  if (st != ARNFP8_OK) return st;
+  st = check_scalars(eps, weight_offset, scale_ub, true);
+  if (st != ARNFP8_OK) return st;
+  const int c16 = (int)(cols / 8);
+  int parts = opt ? opt->parts : 0;
+  if (parts < 0 || parts > kSplitSlots) return ARNFP8_BAD_CONFIG;
+  if (parts > 0 && c16 > 1024 * parts) return ARNFP8_BAD_CONFIG;
+  if (rows == 0) return ARNFP8_OK;
+  SplitArgs a;
+  {
+    RowArgs r;
+    st = prepare_fused(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                       weight_offset, scale_ub, rows, cols, P, &r);
+    if (st != ARNFP8_OK) return st;
+    // A part may re-read a late partner's residual input, so it must stay
+    // unmodified: no in-place update on this path.
+    if (residual_in != nullptr && residual_in == residual_out) return ARNFP8_ALIAS;
+    a.in = r.in;
+    a.res_in = r.res_in;
+    a.res_out = r.res_out;
+    a.out = r.out;
+    a.scales = r.scales;
+    a.gamma = r.gamma;
+    a.eps = r.eps;
+    a.woff = r.woff;
+    a.ub = r.ub;
+    a.inv_cols = r.inv_cols;
+    a.rows = r.rows;
+    a.c16 = r.c16;
+  }
+  if (workspace == nullptr) return ARNFP8_NULL_POINTER;
+  if (!aligned(workspace, 16)) return ARNFP8_MISALIGNED;
+  const int64_t need = arnfp8_split_workspace_bytes(rows);
+  if (need < 0 || workspace_bytes < need) return ARNFP8_BAD_WORKSPACE;
+  {
+    const Range ws{(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)need};
+    const uintptr_t n = (uintptr_t)(rows * cols);
+    for (int p = 0; p < P; ++p)
+      if (overlaps(ws, Range{(uintptr_t)inputs[p], (uintptr_t)inputs[p] + 2 * n})) return ARNFP8_ALIAS;
+    if (residual_in && overlaps(ws, Range{(uintptr_t)residual_in, (uintptr_t)residual_in + 2 * n}))
+      return ARNFP8_ALIAS;
+    if (residual_out && overlaps(ws, Range{(uintptr_t)residual_out, (uintptr_t)residual_out + 2 * n}))
+      return ARNFP8_ALIAS;
+    if (overlaps(ws, Range{(uintptr_t)out_fp8, (uintptr_t)out_fp8 + n}) ||
+        overlaps(ws, Range{(uintptr_t)scales, (uintptr_t)scales + 4 * (uintptr_t)rows}) ||
+        overlaps(ws, Range{(uintptr_t)gamma, (uintptr_t)gamma + 2 * (uintptr_t)cols}))
+      return ARNFP8_ALIAS;
+  }
+  if (parts == 0) {
+    // The largest power of two up to kSplitSlots that keeps the grid within
+    // one workgroup per CU and every part at least one full wave of chunks,
+    // and at least enough parts for 1024 lanes.  Measured on MI355X (graph
+    // replay, inputs out of cache): one row of 8192 columns, P = 8, in 8
+    // parts 4.71 against 5.89 us in one workgroup; 128 rows in 2 parts 7.40
+    // against 7.77 us; 4 rows of 256 columns in 8 parts of 4 chunks 5.76
+    // against 2.89 us (the exchange is then all overhead).
+    const int64_t cus = device_cus();
+    parts = 1;
+    while (parts * 2 <= kSplitSlots && rows * parts * 2 <= cus && c16 >= 64 * parts * 2) parts *= 2;
+    while (c16 > 1024 * parts && parts < kSplitSlots) parts *= 2;
+    if (c16 > 1024 * parts) return ARNFP8_BAD_CONFIG;
+  }
+  if (rows * parts > (int64_t)INT32_MAX) return ARNFP8_BAD_SHAPE;
+  a.ws = (unsigned long long *)workspace;
+  a.parts = parts;
+  a.cpp = (c16 + parts - 1) / parts;
+  const int spin = opt ? opt->spin_polls : 0;
+  a.spin_polls = spin == 0 ? 32768 : (spin < 0 ? -1 : spin);
+  const int threads = (a.cpp + 63) / 64 * 64;
+  return launch(split_table(P, residual_in != nullptr, residual_out != nullptr),
+                dim3((unsigned)(rows * parts)), dim3(threads), stream, a);
+}
+
 extern "C" int arnfp8_convert_f32(const float *in, void *out, int64_t n, int format,
                                   hipStream_t stream) {
   if (format != ARNFP8_FMT_E4M3FN && format != ARNFP8_FMT_E5M2 && format != ARNFP8_CVT_BF16)
@@ -440,6 +525,7 @@ extern "C" const char *arnfp8_status_string(int status) {
     case ARNFP8_BAD_FORMAT: return "unknown output format";
     case ARNFP8_BAD_SCALAR:
       return "bad scalar: eps must be finite and >= 0, weight_offset finite, scale_ub > 0";
+    case ARNFP8_BAD_WORKSPACE: return "workspace smaller than arnfp8_split_workspace_bytes(rows)";
     default: return "unknown status";
   }
 }

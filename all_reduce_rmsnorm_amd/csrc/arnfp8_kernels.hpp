@@ -335,6 +335,27 @@ struct RowArgs {
   int c16;  // 16-byte chunks per row
 };
 
+// Arguments of the split-row kernel (arnfp8_split.hip): the row kernel's, plus
+// the exchange workspace ([rows][kSplitSlots][2] 64-bit words), the parts per
+// row, the chunks per part and the bound of the wait for a partner's words.
+constexpr int kSplitSlots = 8;  // most parts a row can be split into
+struct SplitArgs {
+  Slabs in;
+  const u32x4 *res_in;
+  u32x4 *res_out;
+  u32x2 *out;
+  float *scales;
+  const u32x4 *gamma;
+  unsigned long long *ws;
+  float eps, woff, ub;
+  float inv_cols;
+  int64_t rows;
+  int c16;
+  int parts;       // workgroups per row, 1..kSplitSlots
+  int cpp;         // chunks per part, ceil(c16 / parts)
+  int spin_polls;  // polls of a partner's words before computing its pair here
+};
+
 // Loads in flight per lane in the statistics pass: chunks are processed in
 // groups of G whose P slab loads (plus residual and gamma) are all issued
 // before any of them is consumed.

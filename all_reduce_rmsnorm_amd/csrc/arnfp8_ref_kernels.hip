@@ -20,7 +20,8 @@
 //   arnref_exchange  the cost of one exchange between workgroups: groups of S
 //                 workgroups each publish one 64-bit word (a 32-bit payload and
 //                 a 32-bit count) with a relaxed device-scope atomic store and
-//                 wait until every partner's word carries the same count, as a
+//                 wait, one lane per partner, until every partner's word
+//                 carries the same count, as a
 //                 row split across S workgroups would trade its row statistics.
 //                 Each word has a single writer whose count goes up by one per
 //                 launch, so partners stay in step across launches and graph
@@ -146,27 +147,27 @@ __global__ __launch_bounds__(64) void exchange_kernel(unsigned long long *words,
     first = (b / S) * S;
     step = 1;
   }
+  // Lane 0 publishes; lane j < S then polls partner j, all partners at once.
+  unsigned long long *mine = words + b;
+  const unsigned long long old = __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned count = (unsigned)(old >> 32) + 1u;
   if (threadIdx.x == 0) {
-    unsigned long long *mine = words + b;
-    const unsigned long long old =
-        __hip_atomic_load(mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned count = (unsigned)(old >> 32) + 1u;
     const unsigned long long word = ((unsigned long long)count << 32) | (unsigned)b;
     __hip_atomic_store(mine, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool late = false;
-    for (int j = 0; j < S; ++j) {
-      unsigned long long *theirs = words + first + j * step;
-      if (theirs == mine) continue;
+  }
+  const int j = threadIdx.x;
+  if (j < S) {
+    unsigned long long *theirs = words + first + j * step;
+    if (theirs != mine) {
       int spins = 0;
       while ((unsigned)(__hip_atomic_load(theirs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >>
                         32) != count) {
         if (++spins == kSpinLimit) {
-          late = true;
+          atomicAdd(timeouts, 1u);
           break;
         }
       }
     }
-    if (late) atomicAdd(timeouts, 1u);
   }
 }
 

@@ -16,6 +16,12 @@ RowKernel row_table_e4m3(int P, int vpt, bool res_in, bool res_out, bool sc1);
 RowKernel row_table_e5m2(int P, int vpt, bool res_in, bool res_out, bool sc1);
 RowKernel row_table_mxfp8(int P, int vpt, bool res_in, bool res_out, bool sc1);
 
+typedef void (*SplitKernel)(SplitArgs);
+
+// The split-row kernel instance for (P in 1..8, residual read, residual
+// written); e4m3fn output (arnfp8_split.hip).
+SplitKernel split_table(int P, bool res_in, bool res_out);
+
 // Builds one format's table from its kernel template instances.
 template <int FMT>
 struct RowTable {

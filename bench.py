@@ -62,6 +62,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_kernels.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_tables.hpp"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8.hip"),
+                  os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_split.hip"),
                   os.path.join(ROOT, "include", "arnfp8.h"),
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
 
@@ -219,6 +220,24 @@ def call_on(w, d, arn, launch=None):
                                   d["scales"], d["gamma"], w.eps, w.weight_offset, w.scale_ub)
 
 
+def split_call_on(w, d, arn, workspace):
+    """One arnfp8_run_split call of workload `w` on the buffers of `d` (the
+    automatic number of parts), trading statistics through `workspace`."""
+    return lambda: arn.arnfp8_run_split(d["inputs"], d["residual"], d["res_out"], d["out"],
+                                        d["scales"], d["gamma"], w.eps, w.weight_offset,
+                                        w.scale_ub, workspace=workspace)
+
+
+def split_parts(w, cus):
+    """The automatic parts per row of arnfp8_run_split (for the record)."""
+    parts = 1
+    while parts * 2 <= 8 and w.rows * parts * 2 <= cus and w.cols // 8 >= 64 * parts * 2:
+        parts *= 2
+    while w.cols // 8 > 1024 * parts and parts < 8:
+        parts *= 2
+    return parts
+
+
 def step_fn(w, d, arn):
     """One step of workload `w`, each call writing the next output set."""
     return rotating([call_on(w, dict(d, **o), arn) for o in d["outs"]])
@@ -329,6 +348,16 @@ def latency_figures(w, torch, arn, dev, flush, khash, calls=100, nwin=64):
         fs1 = [call_on(w, d, arn, launch={"vpt": 1}) for d in wins]
         r["one_chunk_per_lane_cold_us_per_call"] = round(
             graph_us_per_call(torch, fs1, flush=flush), 3)
+    if not w.sum_only and not w.in_place:
+        # The same calls with each row split across workgroups that trade
+        # their statistics (arnfp8_run_split; not for an in-place residual).
+        ws = torch.zeros((arn.arnfp8_split_workspace_bytes(w.rows) // 8,), dtype=torch.int64,
+                         device=dev)
+        fsp = [split_call_on(w, d, arn, ws) for d in wins]
+        r["split_parts"] = split_parts(w, torch.cuda.get_device_properties(dev).multi_processor_count)
+        r["split_warm_us_per_call"] = round(graph_us_per_call(torch, [fsp[0]] * calls), 3)
+        r["split_cold_us_per_call"] = round(graph_us_per_call(torch, fsp, flush=flush), 3)
+        del ws, fsp
     del wins, fs
     torch.cuda.empty_cache()
     return r
@@ -456,6 +485,10 @@ def decode_breakdown(w, torch, arn, dev, flush, nwin=64):
             2 * w.cols, threads, vpt, cur()))),
         "fused": lambda k: call_on(w, wins[k], arn, launch=launch),
     }
+    if not w.in_place:
+        ws = torch.zeros((arn.arnfp8_split_workspace_bytes(w.rows) // 8,), dtype=torch.int64,
+                         device=dev)
+        kinds["fused_split_rows"] = lambda k: split_call_on(w, wins[k], arn, ws)
     # The same bytes spread over `parts` times as many workgroups, each
     # reading (and writing) 1/parts of a row: what splitting rows across
     # workgroups could save on the memory side, before the cost of exchanging

@@ -110,6 +110,9 @@ extern "C" {
  * stabilising term, weight_offset an additive offset of gamma, scale_ub the
  * upper bound of the scale clamp). */
 #define ARNFP8_BAD_SCALAR 10
+/* The arnfp8_run_split workspace is missing space: fewer than
+ * arnfp8_split_workspace_bytes(rows) bytes (this library's own interface). */
+#define ARNFP8_BAD_WORKSPACE 11
 
 /*
  * arnfp8_run -- the fused epilogue.  For every row i and column j:
@@ -223,6 +226,57 @@ int arnfp8_run_fmt(const void *const *inputs, const void *residual_in, void *res
                    void *out_fp8, void *scales, const void *gamma, float eps,
                    float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
                    int out_format, hipStream_t stream, const arnfp8_launch *opt);
+
+/*
+ * Split rows (small batches and one token).  TensorRT-LLM PR #19836
+ * (Description) spreads a one-token row of the RESIDUAL_RMS_NORM epilogue over
+ * a cluster of 8 CTAs that trade partial sums.  arnfp8_run_split spreads each
+ * row over `parts` workgroups the same way, so that a row's bytes stream into
+ * several compute units at once; the parts trade their partial (sum h^2,
+ * max |h g|) through `workspace`, one relaxed 64-bit atomic word per value,
+ * and wait for one another (boundedly).
+ *
+ * The result is that of arnfp8_run (e4m3fn output) for the same arguments,
+ * within the operation's tolerance: bf16 outputs are identical, scales and
+ * codes may differ in the last bits, as between launch shapes (the sum of
+ * squares is reduced per part, then over the parts in order).  Results are
+ * deterministic, also when a part runs out of waiting: it then computes the
+ * late partner's partial itself, from the inputs, bitwise as the partner does.
+ * For that reason residual_out must not be residual_in (ARNFP8_ALIAS): the
+ * late partner's residual input must still be there to be read.
+ *
+ * workspace  device memory of at least arnfp8_split_workspace_bytes(rows)
+ *            bytes, 16-byte aligned, overlapping no input or output, set to
+ *            zero before its first use and then left to the library (it
+ *            keeps per-row counts between calls; any later call of any shape
+ *            may use it).  Calls that may run at the same time (other
+ *            streams) need workspaces of their own.  Else ARNFP8_NULL_POINTER,
+ *            ARNFP8_MISALIGNED, ARNFP8_BAD_WORKSPACE or ARNFP8_ALIAS.
+ * opt        NULL for the automatic choice, else:
+ *   parts      workgroups per row, 1..8 (0: the largest power of two up to 8
+ *              with rows * parts <= the compute units and at least 64 chunks
+ *              of 16 bytes per part, at least 1); a part holds
+ *              ceil(cols / 8 / parts) chunks, at most 1024 (else
+ *              ARNFP8_BAD_CONFIG)
+ *   spin_polls polls of a partner's words before its partial is computed
+ *              locally: 0 for the default (32768), -1 for none at once (the
+ *              fallback alone, for testing), else the count
+ * Every other argument and rule is that of arnfp8_run.
+ */
+typedef struct arnfp8_split_opts {
+  int parts;
+  int spin_polls;
+} arnfp8_split_opts;
+
+/* Workspace bytes arnfp8_run_split needs for `rows` rows (128 per row), or -1
+ * for rows < 0. */
+int64_t arnfp8_split_workspace_bytes(int64_t rows);
+
+int arnfp8_run_split(const void *const *inputs, const void *residual_in, void *residual_out,
+                     void *out_fp8, float *scales, const void *gamma, float eps,
+                     float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
+                     void *workspace, int64_t workspace_bytes, hipStream_t stream,
+                     const arnfp8_split_opts *opt);
 
 /*
  * arn_sum_bf16 -- the reduction alone: out = s as defined for arnfp8_run.

@@ -38,6 +38,18 @@ int main(void) {
   expect("bad threads", arnfp8_run_ex(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, NULL, &opt), ARNFP8_BAD_CONFIG);
   expect("bad format", arnfp8_run_fmt(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, 42, NULL, NULL), ARNFP8_BAD_FORMAT);
   expect("bad share", arnfp8_run_share(inputs, NULL, NULL, out, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, 4, 4, NULL), ARNFP8_BAD_SHARE);
+  {
+    arnfp8_split_opts sopt = {9, 0};
+    void *ws = (void *)(base + 500 * mb);
+    expect("split bad parts", arnfp8_run_split(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, ws, 512, NULL, &sopt), ARNFP8_BAD_CONFIG);
+    sopt.parts = 2;
+    expect("split small workspace", arnfp8_run_split(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, ws, 511, NULL, &sopt), ARNFP8_BAD_WORKSPACE);
+    expect("split rows 0", arnfp8_run_split(inputs, NULL, NULL, NULL, NULL, NULL, 1e-6f, 0.0f, 1.0f, 0, 256, 2, NULL, 0, NULL, &sopt), ARNFP8_OK);
+    if (arnfp8_split_workspace_bytes(4) != 512) {
+      printf("FAIL split workspace bytes\n");
+      ++failures;
+    }
+  }
   expect("sum bad shape", arn_sum_bf16(inputs, out, 4, 7, 2, NULL), ARNFP8_BAD_SHAPE);
   expect("convert bad n", arnfp8_convert_f32((const float *)base, out, 12, ARNFP8_FMT_E4M3FN, NULL), ARNFP8_BAD_SHAPE);
   if (arnfp8_stage_bytes(8192, 7168, 8) != 7344128) {

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER_DIR = os.path.join(ROOT, "include")
 
 OK, NULLP, MISALIGNED, BAD_SHAPE, BAD_P, ALIAS = 0, 1, 2, 3, 4, 5
-BAD_SCALAR = 10
+BAD_SCALAR, BAD_WORKSPACE = 10, 11
 
 
 @pytest.fixture(scope="module")
@@ -64,7 +64,7 @@ def test_library_is_built_for_gfx950():
 def test_status_strings(L):
     import all_reduce_rmsnorm_amd as arn
 
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = arn.arnfp8_status_string(code)
         assert s and s != "unknown status"
     assert arn.arnfp8_status_string(99) == "unknown status"
@@ -307,3 +307,51 @@ def test_good_scalar_edges_are_accepted(L):
     for eps, woff, ub in ((0.0, 0.0, 1.0), (1e-6, 0.0, INF), (3e38, -3e38, 1e-30)):
         assert L.arnfp8_run(_arr(x0, x1), None, None, BASE + 100 * MB, BASE + 200 * MB,
                             BASE + 300 * MB, eps, woff, ub, 0, 256, 2, None) == OK
+
+
+def test_split_workspace_bytes(L):
+    """Two 64-bit words for each of 8 slots per row; negative or overflowing
+    row counts give -1."""
+    assert L.arnfp8_split_workspace_bytes(0) == 0
+    assert L.arnfp8_split_workspace_bytes(1) == 128
+    assert L.arnfp8_split_workspace_bytes(37) == 37 * 128
+    assert L.arnfp8_split_workspace_bytes(-1) == -1
+    assert L.arnfp8_split_workspace_bytes(1 << 60) == -1
+
+
+def test_split_validation_codes(L):
+    """arnfp8_run_split refuses before any launch: bad shapes, scalars and part
+    counts first (also at rows = 0), then the buffers, then the workspace."""
+    import all_reduce_rmsnorm_amd as arn
+
+    x0, x1 = BASE, BASE + 10 * MB
+    out, sc, g = BASE + 100 * MB, BASE + 200 * MB, BASE + 300 * MB
+    ws = BASE + 500 * MB
+
+    def split(rows=4, cols=1024, res_in=None, res_out=None, workspace=ws, wbytes=None,
+              parts=2, eps=1e-6, ub=1.0, inputs=(x0, x1), gamma=g):
+        wbytes = 128 * max(rows, 0) if wbytes is None else wbytes
+        opt = arn.SplitOpts(parts=parts, spin_polls=0)
+        return L.arnfp8_run_split(_arr(*inputs), res_in, res_out, out, sc, gamma, eps, 0.0, ub,
+                                  rows, cols, len(inputs), workspace, wbytes, None,
+                                  ctypes.byref(opt))
+
+    for rows in (0, 4):
+        assert split(rows=rows, cols=12) == BAD_SHAPE
+        assert split(rows=rows, eps=-1.0) == BAD_SCALAR
+        assert split(rows=rows, ub=0.0) == BAD_SCALAR
+        assert split(rows=rows, parts=9) == 7
+        assert split(rows=rows, parts=-1) == 7
+        assert split(rows=rows, cols=65536, parts=1) == 7  # 8192 chunks > 1024 lanes
+    assert split(inputs=()) == BAD_P
+    assert split(rows=0, workspace=None) == OK
+    assert split(gamma=None) == NULLP
+    assert split(workspace=None) == NULLP
+    assert split(workspace=ws + 8) == MISALIGNED
+    assert split(wbytes=4 * 128 - 8) == BAD_WORKSPACE
+    r = BASE + 400 * MB
+    assert split(res_in=r, res_out=r) == ALIAS            # no in-place residual
+    assert split(workspace=x1 + 1024) == ALIAS            # workspace on an input
+    assert split(workspace=out + 16) == ALIAS             # workspace on the output
+    assert split(workspace=sc - 64) == ALIAS              # workspace runs into the scales
+    assert split(res_out=r, workspace=r + 4 * 1024 * 2 - 16) == ALIAS
