@@ -407,12 +407,23 @@ extern "C" int64_t arnfp8_split_workspace_bytes(int64_t rows) {
   return rows * 2 * kSplitSlots * (int64_t)sizeof(unsigned long long);
 }
 
-extern "C" int arnfp8_run_split(const void *const *inputs, const void *residual_in,
-                                void *residual_out, void *out_fp8, float *scales,
-                                const void *gamma, float eps, float weight_offset, float scale_ub,
-                                int64_t rows, int64_t cols, int P, void *workspace,
-                                int64_t workspace_bytes, hipStream_t stream,
-                                const arnfp8_split_opts *opt) {
+namespace {
+
+// A validated split call: the kernel, its arguments and its launch shape.
+struct SplitCall {
+  SplitKernel kernel;
+  SplitArgs args;
+  dim3 grid, block;
+};
+
+// Validates a split call in the documented order and fills `call`.  Returns
+// ARNFP8_OK with call->kernel == nullptr when there is nothing to launch
+// (rows == 0); the workspace is only looked at when there is.
+int prepare_split(const void *const *inputs, const void *residual_in, void *residual_out,
+                  void *out_fp8, float *scales, const void *gamma, float eps, float weight_offset,
+                  float scale_ub, int64_t rows, int64_t cols, int P, void *workspace,
+                  int64_t workspace_bytes, const arnfp8_split_opts *opt, SplitCall *call) {
+  call->kernel = nullptr;
   int st = check_shape(rows, cols, P);
   if (st != ARNFP8_OK) return st;
   st = check_scalars(eps, weight_offset, scale_ub, true);
@@ -422,7 +433,7 @@ extern "C" int arnfp8_run_split(const void *const *inputs, const void *residual_
   if (parts < 0 || parts > kSplitSlots) return ARNFP8_BAD_CONFIG;
   if (parts > 0 && c16 > 1024 * parts) return ARNFP8_BAD_CONFIG;
   if (rows == 0) return ARNFP8_OK;
-  SplitArgs a;
+  SplitArgs &a = call->args;
   {
     RowArgs r;
     st = prepare_fused(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
@@ -482,9 +493,26 @@ extern "C" int arnfp8_run_split(const void *const *inputs, const void *residual_
   a.cpp = (c16 + parts - 1) / parts;
   const int spin = opt ? opt->spin_polls : 0;
   a.spin_polls = spin == 0 ? 32768 : (spin < 0 ? -1 : spin);
-  const int threads = (a.cpp + 63) / 64 * 64;
-  return launch(split_table(P, residual_in != nullptr, residual_out != nullptr),
-                dim3((unsigned)(rows * parts)), dim3(threads), stream, a);
+  call->grid = dim3((unsigned)(rows * parts));
+  call->block = dim3((a.cpp + 63) / 64 * 64);
+  call->kernel = split_table(P, residual_in != nullptr, residual_out != nullptr);
+  return ARNFP8_OK;
+}
+
+}  // namespace
+
+extern "C" int arnfp8_run_split(const void *const *inputs, const void *residual_in,
+                                void *residual_out, void *out_fp8, float *scales,
+                                const void *gamma, float eps, float weight_offset, float scale_ub,
+                                int64_t rows, int64_t cols, int P, void *workspace,
+                                int64_t workspace_bytes, hipStream_t stream,
+                                const arnfp8_split_opts *opt) {
+  SplitCall c;
+  const int st = prepare_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                               weight_offset, scale_ub, rows, cols, P, workspace,
+                               workspace_bytes, opt, &c);
+  if (st != ARNFP8_OK || c.kernel == nullptr) return st;
+  return launch(c.kernel, c.grid, c.block, stream, c.args);
 }
 
 extern "C" int arnfp8_convert_f32(const float *in, void *out, int64_t n, int format,
