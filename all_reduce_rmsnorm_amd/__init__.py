@@ -22,7 +22,8 @@ __all__ = [
     "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW", "arnfp8_stage_bytes",
     "arnfp8_run_share", "SIMD_WIDTH", "arnfp8_run_fmt", "FMT_E4M3FN", "FMT_E5M2", "FMT_MXFP8",
     "CVT_BF16", "arnfp8_convert_f32", "STORES_AUTO", "STORES_NT", "STORES_SC1",
-    "SplitOpts", "arnfp8_split_workspace_bytes", "arnfp8_run_split",
+    "SplitOpts", "arnfp8_split_workspace_bytes", "arnfp8_run_split", "arnfp8_run_split_noalloc",
+    "NOALLOC_MAX_ROWS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,7 @@ _LIB_PATH = os.path.join(_PKG, "libarnfp8.so")
 
 MAX_P = 8
 MAX_COLS = 65536
+NOALLOC_MAX_ROWS = 4096  # rows of the allocation-free split call (ARNFP8_NOALLOC_MAX_ROWS)
 STATUS = {
     0: "ARNFP8_OK", 1: "ARNFP8_NULL_POINTER", 2: "ARNFP8_MISALIGNED", 3: "ARNFP8_BAD_SHAPE",
     4: "ARNFP8_BAD_P", 5: "ARNFP8_ALIAS", 6: "ARNFP8_HIP_ERROR", 7: "ARNFP8_BAD_CONFIG",
@@ -116,6 +118,10 @@ def library() -> ctypes.CDLL:
         L.arnfp8_run_split.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int,
                                        vp, i64, vp, ctypes.POINTER(SplitOpts)]
+        L.arnfp8_run_split_noalloc.restype = ctypes.c_int
+        L.arnfp8_run_split_noalloc.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp,
+                                               ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                               i64, i64, ctypes.c_int, vp, vp]
         L.arn_sum_bf16.restype = ctypes.c_int
         L.arn_sum_bf16.argtypes = [ctypes.POINTER(vp), vp, i64, i64, ctypes.c_int, vp]
         L.arnfp8_status_string.restype = ctypes.c_char_p
@@ -328,6 +334,28 @@ def arnfp8_run_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, 
                                     rows, cols, P, ws, int(workspace_bytes), _stream(stream), opt)
     if st != 0:
         raise ArnFp8Error("arnfp8_run_split", st)
+
+
+def arnfp8_run_split_noalloc(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                             weight_offset, scale_ub, rows=None, cols=None, P=None, stream=None,
+                             opts=None) -> None:
+    """``arnfp8_run_split`` with the library's own per-device workspace (at
+    most ``NOALLOC_MAX_ROWS`` rows): allocates nothing.  Calls that may run at
+    the same time on one device race (they share that workspace)."""
+    rows, cols, P = _shape(inputs, rows, cols, P)
+    if isinstance(opts, dict):
+        opts = SplitOpts(**opts)
+    opt = ctypes.byref(opts) if opts is not None else None
+    n = rows * cols
+    ptrs = (_ptr_array(inputs, 2 * n), _ptr(residual_in, _BF16, "residual_in", 2 * n),
+            _ptr(residual_out, _BF16, "residual_out", 2 * n), _ptr(out_fp8, _FP8, "out_fp8", n),
+            _ptr(scales, _F32, "scales", 4 * rows), _ptr(gamma, _BF16, "gamma", 2 * cols))
+    _on_device(inputs=inputs, residual_in=residual_in, residual_out=residual_out,
+               out_fp8=out_fp8, scales=scales, gamma=gamma)
+    st = library().arnfp8_run_split_noalloc(*ptrs, float(eps), float(weight_offset),
+                                            float(scale_ub), rows, cols, P, _stream(stream), opt)
+    if st != 0:
+        raise ArnFp8Error("arnfp8_run_split_noalloc", st)
 
 
 def arnfp8_convert_f32(inp, out, fmt, n=None, stream=None) -> None:

@@ -15,6 +15,7 @@
 
 #include <atomic>
 #include <cfloat>
+#include <mutex>
 
 #include "arnfp8.h"
 #include "arnfp8_kernels.hpp"
@@ -515,6 +516,89 @@ extern "C" int arnfp8_run_split(const void *const *inputs, const void *residual_
   return launch(c.kernel, c.grid, c.block, stream, c.args);
 }
 
+// ---- allocation-free split rows -------------------------------------------
+//
+// The workspace of arnfp8_run_split_noalloc is this device array: 128 bytes
+// per row for up to ARNFP8_NOALLOC_MAX_ROWS rows (512 KiB), held by every
+// device the library runs on until the process ends.  Host code never uses
+// the array's name as an address: the address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and kept in scratch_ptr.
+
+static __device__ __align__(256) unsigned long long
+    scratch[ARNFP8_NOALLOC_MAX_ROWS * 2 * arnfp8::kSplitSlots];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int64_t kScratchWords = ARNFP8_NOALLOC_MAX_ROWS * 2 * arnfp8::kSplitSlots;
+
+std::atomic<unsigned long long *> scratch_ptr[kMaxDevices];
+std::atomic<bool> scratch_cleared[kMaxDevices];
+std::mutex scratch_setup;
+
+// Sets every word of the array to zero (a kernel, not a memset, so that it
+// may also be recorded into a graph).
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned long long *p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0ull;
+}
+
+// The current device's index and its copy of the array.
+int scratch_for_current_device(int *dev, unsigned long long **ptr) {
+  if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= kMaxDevices) return ARNFP8_HIP_ERROR;
+  unsigned long long *p = scratch_ptr[*dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(scratch_setup);
+    p = scratch_ptr[*dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      void *q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+        return ARNFP8_HIP_ERROR;
+      p = (unsigned long long *)q;
+      scratch_ptr[*dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return ARNFP8_OK;
+}
+
+}  // namespace
+
+extern "C" int arnfp8_run_split_noalloc(const void *const *inputs, const void *residual_in,
+                                        void *residual_out, void *out_fp8, float *scales,
+                                        const void *gamma, float eps, float weight_offset,
+                                        float scale_ub, int64_t rows, int64_t cols, int P,
+                                        hipStream_t stream, const arnfp8_split_opts *opt) {
+  int st = check_shape(rows, cols, P);
+  if (st != ARNFP8_OK) return st;
+  if (rows > ARNFP8_NOALLOC_MAX_ROWS) return ARNFP8_BAD_WORKSPACE;
+  SplitCall c;
+  if (rows == 0)  // validation only; nothing is launched and no device is touched
+    return prepare_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                         weight_offset, scale_ub, rows, cols, P, nullptr, 0, opt, &c);
+  int dev = 0;
+  unsigned long long *ws = nullptr;
+  st = scratch_for_current_device(&dev, &ws);
+  if (st != ARNFP8_OK) return st;
+  st = prepare_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                     weight_offset, scale_ub, rows, cols, P, ws,
+                     kScratchWords * (int64_t)sizeof(unsigned long long), opt, &c);
+  if (st != ARNFP8_OK) return st;
+  if (!scratch_cleared[dev].load(std::memory_order_acquire)) {
+    // The per-row counts must start equal: clear the whole array once, ahead
+    // of the first launch on this device.  Under graph capture (or if the
+    // capture state cannot be read) the clear is recorded with the call and
+    // the device stays marked as not cleared, so the next call clears again.
+    st = launch(zero_words_kernel, dim3(256), dim3(256), stream, ws, kScratchWords);
+    if (st != ARNFP8_OK) return st;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
+    if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone)
+      scratch_cleared[dev].store(true, std::memory_order_release);
+  }
+  return launch(c.kernel, c.grid, c.block, stream, c.args);
+}
+
 extern "C" int arnfp8_convert_f32(const float *in, void *out, int64_t n, int format,
                                   hipStream_t stream) {
   if (format != ARNFP8_FMT_E4M3FN && format != ARNFP8_FMT_E5M2 && format != ARNFP8_CVT_BF16)
@@ -553,7 +637,9 @@ extern "C" const char *arnfp8_status_string(int status) {
     case ARNFP8_BAD_FORMAT: return "unknown output format";
     case ARNFP8_BAD_SCALAR:
       return "bad scalar: eps must be finite and >= 0, weight_offset finite, scale_ub > 0";
-    case ARNFP8_BAD_WORKSPACE: return "workspace smaller than arnfp8_split_workspace_bytes(rows)";
+    case ARNFP8_BAD_WORKSPACE:
+      return "workspace too small: fewer than arnfp8_split_workspace_bytes(rows) bytes, or more "
+             "than ARNFP8_NOALLOC_MAX_ROWS rows for the allocation-free call";
     default: return "unknown status";
   }
 }

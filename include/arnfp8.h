@@ -110,8 +110,10 @@ extern "C" {
  * stabilising term, weight_offset an additive offset of gamma, scale_ub the
  * upper bound of the scale clamp). */
 #define ARNFP8_BAD_SCALAR 10
-/* The arnfp8_run_split workspace is missing space: fewer than
- * arnfp8_split_workspace_bytes(rows) bytes (this library's own interface). */
+/* The split workspace is missing space: fewer than
+ * arnfp8_split_workspace_bytes(rows) bytes for arnfp8_run_split, more than
+ * ARNFP8_NOALLOC_MAX_ROWS rows for arnfp8_run_split_noalloc (this library's
+ * own interface). */
 #define ARNFP8_BAD_WORKSPACE 11
 
 /*
@@ -277,6 +279,35 @@ int arnfp8_run_split(const void *const *inputs, const void *residual_in, void *r
                      float weight_offset, float scale_ub, int64_t rows, int64_t cols, int P,
                      void *workspace, int64_t workspace_bytes, hipStream_t stream,
                      const arnfp8_split_opts *opt);
+
+/*
+ * arnfp8_run_split_noalloc -- arnfp8_run_split for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing and takes no
+ * workspace: the workspace is a device array of this library, 128 bytes per
+ * row for up to ARNFP8_NOALLOC_MAX_ROWS rows (512 KiB), which every device
+ * the library runs on holds until the process ends.
+ *
+ *   rows       at most ARNFP8_NOALLOC_MAX_ROWS, else ARNFP8_BAD_WORKSPACE
+ *              (checked after the shape, before everything else)
+ *   stream     a stream of the current device; the array used is that
+ *              device's.  The first call with rows > 0 on a device looks the
+ *              array's address up and clears the array on `stream`, before
+ *              its own launch.
+ * Every call on a device shares that device's array and leaves its per-row
+ * counts for the next call, of any shape: calls that may run at the same time
+ * on one device (other streams, other threads) race and give wrong results;
+ * order them (one stream, or events).  Every other argument, rule and status
+ * is that of arnfp8_run_split, whose kernels it launches; outputs are bitwise
+ * those of arnfp8_run_split with the same arguments and options.
+ */
+#define ARNFP8_NOALLOC_MAX_ROWS 4096
+
+int arnfp8_run_split_noalloc(const void *const *inputs, const void *residual_in,
+                             void *residual_out, void *out_fp8, float *scales, const void *gamma,
+                             float eps, float weight_offset, float scale_ub, int64_t rows,
+                             int64_t cols, int P, hipStream_t stream,
+                             const arnfp8_split_opts *opt);
 
 /*
  * arn_sum_bf16 -- the reduction alone: out = s as defined for arnfp8_run.

@@ -45,6 +45,8 @@ int main(void) {
     sopt.parts = 2;
     expect("split small workspace", arnfp8_run_split(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 1.0f, 4, 256, 2, ws, 511, NULL, &sopt), ARNFP8_BAD_WORKSPACE);
     expect("split rows 0", arnfp8_run_split(inputs, NULL, NULL, NULL, NULL, NULL, 1e-6f, 0.0f, 1.0f, 0, 256, 2, NULL, 0, NULL, &sopt), ARNFP8_OK);
+    expect("noalloc too many rows", arnfp8_run_split_noalloc(inputs, NULL, NULL, out, scales, gamma, 1e-6f, 0.0f, 1.0f, ARNFP8_NOALLOC_MAX_ROWS + 1, 256, 2, NULL, &sopt), ARNFP8_BAD_WORKSPACE);
+    expect("noalloc rows 0", arnfp8_run_split_noalloc(inputs, NULL, NULL, NULL, NULL, NULL, 1e-6f, 0.0f, 1.0f, 0, 256, 2, NULL, &sopt), ARNFP8_OK);
     if (arnfp8_split_workspace_bytes(4) != 512) {
       printf("FAIL split workspace bytes\n");
       ++failures;

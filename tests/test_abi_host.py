@@ -355,3 +355,25 @@ def test_split_validation_codes(L):
     assert split(workspace=out + 16) == ALIAS             # workspace on the output
     assert split(workspace=sc - 64) == ALIAS              # workspace runs into the scales
     assert split(res_out=r, workspace=r + 4 * 1024 * 2 - 16) == ALIAS
+
+
+def test_noalloc_split_refuses_before_touching_the_device(L):
+    """Rows beyond ARNFP8_NOALLOC_MAX_ROWS give BAD_WORKSPACE after the shape
+    check; rows = 0 validates and returns OK (no device is looked at)."""
+    import all_reduce_rmsnorm_amd as arn
+
+    x0, x1 = BASE, BASE + 10 * MB
+    out, sc, g = BASE + 100 * MB, BASE + 200 * MB, BASE + 300 * MB
+
+    def noalloc(rows, cols=256, eps=1e-6, parts=0):
+        opt = arn.SplitOpts(parts=parts, spin_polls=0)
+        return L.arnfp8_run_split_noalloc(_arr(x0, x1), None, None, out, sc, g, eps, 0.0, 1.0,
+                                          rows, cols, 2, None, ctypes.byref(opt))
+
+    assert arn.NOALLOC_MAX_ROWS == 4096
+    assert noalloc(arn.NOALLOC_MAX_ROWS + 1) == BAD_WORKSPACE
+    assert noalloc(arn.NOALLOC_MAX_ROWS + 1, cols=12) == BAD_SHAPE
+    assert noalloc(-1) == BAD_SHAPE
+    assert noalloc(0) == OK
+    assert noalloc(0, eps=-1.0) == BAD_SCALAR
+    assert noalloc(0, parts=9) == 7
