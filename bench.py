@@ -67,17 +67,25 @@ KERNEL_SOURCES = [os.path.join(ROOT, "all_reduce_rmsnorm_amd", "csrc", "arnfp8_k
                   os.path.join(ROOT, "all_reduce_rmsnorm_amd", "build.py")]
 
 
-def kernel_name_of(workload) -> str:
+def kernel_name_of(workload, split=False) -> str:
     """The kernel a workload times: the sum kernel for the sum-only workload,
-    else the fused row kernel."""
+    the split-row kernel for its arnfp8_run_split calls, else the fused row
+    kernel."""
     from all_reduce_rmsnorm_amd import synth
 
+    if split:
+        return "arnfp8_split_kernel"
     return "arn_sum_kernel" if synth.WORKLOADS[workload].sum_only else "arnfp8_row_kernel"
 
 
-def profile_path(workload: str, kind: str) -> str:
+# Small workloads whose arnfp8_run_split calls are profiled too (residual out
+# of place, rows well under one per compute unit).
+SPLIT_PROFILE_WORKLOADS = ["token_p8_1x8192", "unit_offset_p8_128x8192"]
+
+
+def profile_path(workload: str, kind: str, split=False) -> str:
     """profiles/<kernel>_<workload>_<kind>.md, kind "hbm_traffic" or "kernel_trace"."""
-    return os.path.join(PROFILES, f"{kernel_name_of(workload)}_{workload}_{kind}.md")
+    return os.path.join(PROFILES, f"{kernel_name_of(workload, split)}_{workload}_{kind}.md")
 
 
 PMC_SUMMARY = os.path.join(PROFILES, "arnfp8_row_kernel_prefill_p8_8192x7168_hbm_traffic.md")
@@ -357,6 +365,12 @@ def latency_figures(w, torch, arn, dev, flush, khash, calls=100, nwin=64):
         r["split_parts"] = split_parts(w, torch.cuda.get_device_properties(dev).multi_processor_count)
         r["split_warm_us_per_call"] = round(graph_us_per_call(torch, [fsp[0]] * calls), 3)
         r["split_cold_us_per_call"] = round(graph_us_per_call(torch, fsp, flush=flush), 3)
+        sk_us = read_profile(profile_path(w.name, "kernel_trace", True), "mean_us", khash)
+        r["split_kernel_us_trace"] = sk_us
+        r["split_frac_kernel_trace"] = (round(alg / (sk_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                        if sk_us else None)
+        r["split_traffic"] = read_profile(profile_path(w.name, "hbm_traffic", True),
+                                          "traffic_bytes_per_launch", khash)
         del ws, fsp
     del wins, fs
     torch.cuda.empty_cache()
@@ -679,17 +693,21 @@ def cpu_oracle_threaded(w, d, torch, passes=3, max_threads=16):
 
 # ------------------------------------------------------- HBM counters ------
 
-def _kernel_filter(workload):
+def _kernel_filter(workload, split=False):
     """A predicate on rocprofv3 kernel names: the kernel `workload` times
-    (the e4m3fn row kernel with its P, or the sum kernel with its P)."""
+    (the e4m3fn row kernel with its P, the sum kernel with its P, or the
+    split-row kernel with its P)."""
     from all_reduce_rmsnorm_amd import synth
 
     w = synth.WORKLOADS[workload]
-    want = f"arn_sum_kernel<{w.P}," if w.sum_only else f"arnfp8_row_kernel<0, {w.P},"
+    if split:
+        want = f"arnfp8_split_kernel<{w.P},"
+    else:
+        want = f"arn_sum_kernel<{w.P}," if w.sum_only else f"arnfp8_row_kernel<0, {w.P},"
     return lambda name: want in name.replace("(anonymous namespace)::", "")
 
 
-def summarize_pmc(directory: str, out_path: str, workload: str, command: str = ""):
+def summarize_pmc(directory: str, out_path: str, workload: str, command: str = "", split=False):
     """Build the counter summary from rocprofv3 --pmc CSV output under
     `directory` (or under each of a comma-separated list of directories): one
     run with FETCH_SIZE, one with WRITE_SIZE, each holding the workload's
@@ -699,7 +717,7 @@ def summarize_pmc(directory: str, out_path: str, workload: str, command: str = "
     from all_reduce_rmsnorm_amd import synth
 
     w = synth.WORKLOADS[workload]
-    is_kernel = _kernel_filter(workload)
+    is_kernel = _kernel_filter(workload, split)
     per = {}  # counter -> {"kernel": [kib...], "copy": [kib...]}
     dirs = directory.split(",")
     files = sorted(f for d in dirs for f in
@@ -732,11 +750,12 @@ def summarize_pmc(directory: str, out_path: str, workload: str, command: str = "
                      f"{factor:.4f} | {scaled / 1e6:.3f} MB |")
     alg = w.algorithmic_bytes()
     if not command:
-        command = (f"python -u bench.py --profile-workload {workload} --pmc-calib")
+        command = (f"python -u bench.py --profile-workload {workload} --pmc-calib"
+                   + (" --split" if split else ""))
     fetch_dir, write_dir = (dirs + dirs)[:2] if len(dirs) > 1 else (f"{directory}/pmc_fetch",
                                                                   f"{directory}/pmc_write")
     text = "\n".join([
-        f"# HBM traffic of `{kernel_name_of(workload)}` on {workload}",
+        f"# HBM traffic of `{kernel_name_of(workload, split)}` on {workload}",
         "",
         "Counters from two `rocprofv3 --pmc` runs (FETCH_SIZE, then WRITE_SIZE), per",
         "dispatch, scaled by what the same counter reads for a plain copy of",
@@ -746,7 +765,8 @@ def summarize_pmc(directory: str, out_path: str, workload: str, command: str = "
         "",
         f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o fetch -- {command}",
         f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o write -- {command}",
-        f"    python bench.py --summarize-pmc {directory} --workload {workload}",
+        f"    python bench.py --summarize-pmc {directory} --workload {workload}"
+        + (" --split" if split else ""),
         "",
         "| counter | kernel (mean per dispatch) | copy kernel | scale factor | scaled bytes |",
         "|---|---|---|---|---|",
@@ -771,7 +791,7 @@ def _short_name(name: str) -> str:
     return name.split("(")[0]
 
 
-def summarize_ktrace(directory: str, out_path: str, command: str, workload: str):
+def summarize_ktrace(directory: str, out_path: str, command: str, workload: str, split=False):
     """Summarise a rocprofv3 --kernel-trace --stats CSV run: the library's
     kernels, split by launch shape (grid, workgroup), with mean durations;
     the workload's own kernel and launch shape get machine-readable lines."""
@@ -793,7 +813,7 @@ def summarize_ktrace(directory: str, out_path: str, command: str, workload: str)
                 continue
             key = (_short_name(name), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
             shapes[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines = [f"# Kernel trace: `{kernel_name_of(workload)}` on {workload}", "",
+    lines = [f"# Kernel trace: `{kernel_name_of(workload, split)}` on {workload}", "",
              "Command (from the repository root, on one MI355X):", "",
              f"    {command}", "",
              "Per launch shape (grid = total lanes), from the kernel trace:", "",
@@ -813,9 +833,9 @@ def summarize_ktrace(directory: str, out_path: str, command: str, workload: str)
                          f"{float(r['Percentage']):.2f} |")
     # The workload's kernel at its launch shape (grid = min(rows, 65536)
     # workgroups for the row kernel; the shape with the most calls otherwise).
-    is_kernel = _kernel_filter(workload)
+    is_kernel = _kernel_filter(workload, split)
     mine = [(k, v) for k, v in shapes.items() if is_kernel(k[0])]
-    if not w.sum_only:
+    if not w.sum_only and not split:
         wgs = min(w.rows, 65536)
         mine = [(k, v) for k, v in mine if k[1] == wgs * k[2]] or mine
     if not mine:
@@ -833,11 +853,12 @@ def summarize_ktrace(directory: str, out_path: str, command: str, workload: str)
 
 # ------------------------------------------------------ profile workloads --
 
-def profile_workload(name, torch, arn, dev, steps):
+def profile_workload(name, torch, arn, dev, steps, split=False):
     """Only the calls of workload `name`, each on bytes that no earlier call
     touched since the last flush, for rocprofv3 (kernel trace or counters):
     the prefill step with rotating output sets, the share's ranks in turn,
-    and the small workloads on disjoint windows."""
+    and the small workloads on disjoint windows (with `split`, through
+    arnfp8_run_split)."""
     from all_reduce_rmsnorm_amd import synth
 
     if name == SHARE_WORKLOAD:
@@ -857,7 +878,12 @@ def profile_workload(name, torch, arn, dev, steps):
     else:
         w = synth.WORKLOADS[name]
         wins = alloc_windows(w, torch, dev, max(steps, 8))
-        fn = rotating([call_on(w, d, arn) for d in wins])
+        if split:
+            ws = torch.zeros((arn.arnfp8_split_workspace_bytes(w.rows) // 8,), dtype=torch.int64,
+                             device=dev)
+            fn = rotating([split_call_on(w, d, arn, ws) for d in wins])
+        else:
+            fn = rotating([call_on(w, d, arn) for d in wins])
     # The inputs were just written by the generator: flush them out of the
     # caches, so that every profiled call reads its bytes from HBM.
     flush = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
@@ -891,15 +917,18 @@ def main():
     ap.add_argument("--summarize-pmc", metavar="DIR")
     ap.add_argument("--summarize-ktrace", metavar="DIR")
     ap.add_argument("--command", default="", help="the profiled command, for the summary")
+    ap.add_argument("--split", action="store_true",
+                    help="with --profile-workload / --summarize-*: the arnfp8_run_split calls")
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc, profile_path(args.workload, "hbm_traffic"),
-                      args.workload, args.command)
+        summarize_pmc(args.summarize_pmc, profile_path(args.workload, "hbm_traffic", args.split),
+                      args.workload, args.command, args.split)
         return 0
     if args.summarize_ktrace:
-        summarize_ktrace(args.summarize_ktrace, profile_path(args.workload, "kernel_trace"),
-                         args.command, args.workload)
+        summarize_ktrace(args.summarize_ktrace,
+                         profile_path(args.workload, "kernel_trace", args.split), args.command,
+                         args.workload, args.split)
         return 0
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
@@ -928,7 +957,7 @@ def main():
         log(f"pmc calibration copy: {src.numel() * 2} bytes read, {dst.numel() * 2} bytes written")
         del src, dst
     if args.profile_workload:
-        profile_workload(args.profile_workload, torch, arn, dev, args.steps)
+        profile_workload(args.profile_workload, torch, arn, dev, args.steps, args.split)
         return 0
 
     w = synth.WORKLOADS[DEFAULT_WORKLOAD]

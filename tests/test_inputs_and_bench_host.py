@@ -182,3 +182,27 @@ def test_rotating_calls_each_function_in_turn():
     for _ in range(7):
         f()
     assert seen == [0, 1, 2, 0, 1, 2, 0]
+
+
+def test_summarize_pmc_split_picks_the_split_kernel(tmp_path):
+    """With split, the summary counts the split-row kernel's dispatches of the
+    workload's P, not the row kernel's."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    d = tmp_path / "pmc"
+    d.mkdir()
+    hdr = "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n"
+    rows = ('1,"void arnfp8::arn_sum_kernel<1, 4>(x)",{c},1048576\n'
+            '2,"void arnfp8::arnfp8_row_kernel<0, 8, 1, false, true, true>(y)",{c},999\n'
+            '3,"void arnfp8::arnfp8_split_kernel<8, false, true>(arnfp8::SplitArgs)",{c},100\n'
+            '4,"void arnfp8::arnfp8_split_kernel<4, false, true>(arnfp8::SplitArgs)",{c},777\n')
+    (d / "a_counter_collection.csv").write_text(hdr + rows.format(c="FETCH_SIZE"))
+    (d / "b_counter_collection.csv").write_text(hdr + rows.format(c="WRITE_SIZE"))
+    out = tmp_path / "summary.md"
+    bench.summarize_pmc(str(d), str(out), "token_p8_1x8192", split=True)
+    text = out.read_text()
+    assert f"traffic_bytes_per_launch: {int(round(100 * 1024 * 2))}" in text
+    assert "arnfp8_split_kernel" in text and "--split" in text
+    assert bench.profile_path("token_p8_1x8192", "kernel_trace", True).endswith(
+        "arnfp8_split_kernel_token_p8_1x8192_kernel_trace.md")
