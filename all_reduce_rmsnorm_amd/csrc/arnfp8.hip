@@ -410,21 +410,30 @@ extern "C" int64_t arnfp8_split_workspace_bytes(int64_t rows) {
 
 namespace {
 
-// A validated split call: the kernel, its arguments and its launch shape.
+// A validated split call: the kernel, its arguments and its launch shape;
+// with one part per row, the row kernel of arnfp8_run instead.
 struct SplitCall {
   SplitKernel kernel;
   SplitArgs args;
+  RowKernel row_kernel;
+  RowArgs row_args;
   dim3 grid, block;
 };
 
+int launch_split(const SplitCall &c, hipStream_t stream) {
+  if (c.row_kernel != nullptr) return launch(c.row_kernel, c.grid, c.block, stream, c.row_args);
+  return launch(c.kernel, c.grid, c.block, stream, c.args);
+}
+
 // Validates a split call in the documented order and fills `call`.  Returns
-// ARNFP8_OK with call->kernel == nullptr when there is nothing to launch
-// (rows == 0); the workspace is only looked at when there is.
+// ARNFP8_OK with neither kernel set when there is nothing to launch (rows ==
+// 0); the workspace is only looked at when there is.
 int prepare_split(const void *const *inputs, const void *residual_in, void *residual_out,
                   void *out_fp8, float *scales, const void *gamma, float eps, float weight_offset,
                   float scale_ub, int64_t rows, int64_t cols, int P, void *workspace,
                   int64_t workspace_bytes, const arnfp8_split_opts *opt, SplitCall *call) {
   call->kernel = nullptr;
+  call->row_kernel = nullptr;
   int st = check_shape(rows, cols, P);
   if (st != ARNFP8_OK) return st;
   st = check_scalars(eps, weight_offset, scale_ub, true);
@@ -436,7 +445,7 @@ int prepare_split(const void *const *inputs, const void *residual_in, void *resi
   if (rows == 0) return ARNFP8_OK;
   SplitArgs &a = call->args;
   {
-    RowArgs r;
+    RowArgs &r = call->row_args;
     st = prepare_fused(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
                        weight_offset, scale_ub, rows, cols, P, &r);
     if (st != ARNFP8_OK) return st;
@@ -488,6 +497,16 @@ int prepare_split(const void *const *inputs, const void *residual_in, void *resi
     while (c16 > 1024 * parts && parts < kSplitSlots) parts *= 2;
     if (c16 > 1024 * parts) return ARNFP8_BAD_CONFIG;
   }
+  if (parts == 1) {
+    // Nothing to trade: arnfp8_run's kernel and launch shape, and the
+    // workspace is left as it is (its per-row counts stay equal).
+    const RowConfig cfg = pick_row_config(rows, c16, P);
+    call->row_kernel = row_table(ARNFP8_FMT_E4M3FN, P, cfg.vpt, residual_in != nullptr,
+                                 residual_out != nullptr, false);
+    call->grid = dim3(cfg.grid);
+    call->block = dim3(cfg.threads);
+    return ARNFP8_OK;
+  }
   if (rows * parts > (int64_t)INT32_MAX) return ARNFP8_BAD_SHAPE;
   a.ws = (unsigned long long *)workspace;
   a.parts = parts;
@@ -512,8 +531,8 @@ extern "C" int arnfp8_run_split(const void *const *inputs, const void *residual_
   const int st = prepare_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
                                weight_offset, scale_ub, rows, cols, P, workspace,
                                workspace_bytes, opt, &c);
-  if (st != ARNFP8_OK || c.kernel == nullptr) return st;
-  return launch(c.kernel, c.grid, c.block, stream, c.args);
+  if (st != ARNFP8_OK || (c.kernel == nullptr && c.row_kernel == nullptr)) return st;
+  return launch_split(c, stream);
 }
 
 // ---- allocation-free split rows -------------------------------------------
@@ -585,6 +604,7 @@ extern "C" int arnfp8_run_split_noalloc(const void *const *inputs, const void *r
                      weight_offset, scale_ub, rows, cols, P, ws,
                      kScratchWords * (int64_t)sizeof(unsigned long long), opt, &c);
   if (st != ARNFP8_OK) return st;
+  if (c.row_kernel != nullptr) return launch_split(c, stream);  // the array is not used
   if (!scratch_cleared[dev].load(std::memory_order_acquire)) {
     // The per-row counts must start equal: clear the whole array once, ahead
     // of the first launch on this device.  Under graph capture (or if the
@@ -596,7 +616,7 @@ extern "C" int arnfp8_run_split_noalloc(const void *const *inputs, const void *r
     if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone)
       scratch_cleared[dev].store(true, std::memory_order_release);
   }
-  return launch(c.kernel, c.grid, c.block, stream, c.args);
+  return launch_split(c, stream);
 }
 
 extern "C" int arnfp8_convert_f32(const float *in, void *out, int64_t n, int format,

@@ -245,7 +245,11 @@ int arnfp8_run_fmt(const void *const *inputs, const void *residual_in, void *res
  * deterministic, also when a part runs out of waiting: it then computes the
  * late partner's partial itself, from the inputs, bitwise as the partner does.
  * For that reason residual_out must not be residual_in (ARNFP8_ALIAS): the
- * late partner's residual input must still be there to be read.
+ * late partner's residual input must still be there to be read.  With one
+ * part per row (asked for, or the automatic choice at larger batches and for
+ * rows under 128 chunks) there is nothing to trade: the call launches
+ * arnfp8_run's kernel in arnfp8_run's launch shape, with the same result
+ * bits, and leaves the workspace as it is.
  *
  * workspace  device memory of at least arnfp8_split_workspace_bytes(rows)
  *            bytes, 16-byte aligned, overlapping no input or output, set to

@@ -98,8 +98,10 @@ def test_fallback_gives_the_same_bits_as_the_exchange(arn, rows, cols, P, parts)
 
 def test_counts_stay_in_step_across_shapes(arn):
     """One workspace, calls of several row counts and part counts: after each
-    call every slot of every row it touched carries that row's call count,
-    and every result equals the one from a fresh workspace."""
+    call every slot of every row carries the number of calls with two or more
+    parts that touched the row (one part runs the row kernel and leaves the
+    workspace alone), and every result equals the one from a fresh
+    workspace."""
     cols, P = 4096, 4
     ws = _workspace(arn, 64)
     calls = {}
@@ -109,7 +111,7 @@ def test_counts_stay_in_step_across_shapes(arn):
         fresh = _run(arn, xs, res, gamma, True, _workspace(arn, rows), opts=dict(parts=parts))
         for u, v in zip(got, fresh):
             assert torch.equal(u.view(torch.uint8), v.view(torch.uint8)), (rows, parts)
-        for r in range(rows):
+        for r in range(rows if parts > 1 else 0):
             calls[r] = calls.get(r, 0) + 1
         counts = (ws.view(64, 8, 2) >> 32).cpu().numpy()
         for r in range(64):
@@ -197,3 +199,23 @@ def test_refusals_before_launch(arn):
     assert status(opts=dict(parts=-1)) == 7
     torch.cuda.synchronize()
     assert torch.all(out == 0x11) and torch.all(sc == -1.0)
+
+
+@pytest.mark.parametrize("rows,cols,P,parts", [(4, 256, 2, 0), (300, 7168, 8, 0), (9, 4096, 4, 1)])
+def test_one_part_runs_the_row_kernel(arn, rows, cols, P, parts):
+    """One part per row (automatic for rows under 128 chunks and for larger
+    batches, or asked for): the result bits are arnfp8_run's and the workspace
+    is not written."""
+    xs, res, gamma = _case(3 * rows + cols, rows, cols, P, "in_out")
+    ws = torch.full((max(16, arn.arnfp8_split_workspace_bytes(rows)) // 8,), 77, dtype=torch.int64,
+                    device=DEV)
+    got = _run(arn, xs, res, gamma, True, ws, opts=dict(parts=parts))
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=DEV)
+    sc = torch.empty((rows,), dtype=torch.float32, device=DEV)
+    ro = torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)
+    arn.arnfp8_run([x.to(DEV) for x in xs], res.to(DEV), ro, out, sc, gamma.to(DEV), 1e-6, 0.0,
+                   1200.0)
+    torch.cuda.synchronize()
+    for u, v in zip(got, (out, sc, ro)):
+        assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
+    assert torch.all(ws == 77)

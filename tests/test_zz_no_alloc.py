@@ -48,7 +48,7 @@ def _same(a, b):
 
 
 # (rows, cols, P, parts): the second call is smaller than the first.
-CALLS = [(96, 7168, 8, 0), (1, 8192, 8, 0), (4096, 1024, 2, 1), (7, 7176, 3, 4)]
+CALLS = [(96, 7168, 8, 0), (1, 8192, 8, 0), (4096, 1024, 2, 2), (7, 7176, 3, 4)]
 
 
 def test_noalloc_matches_split_with_a_workspace(arn):
