@@ -39,21 +39,32 @@ namespace arnfp8 {
 
 namespace {
 
-// Loads one chunk of the row (P slabs, the residual, gamma), forms h and
-// fl32(h * g), and adds the chunk's share of the statistics when `valid`.
+// One chunk's loads: the P slabs, the residual and gamma.
 template <int P, bool RES_IN>
-__device__ __forceinline__ void split_chunk(const SplitArgs &a, int64_t base, int c, bool valid,
-                                            u32x4 &hv, float hg[8], float &ss, float &mx) {
+struct ChunkIn {
   u32x4 x[P], r, g;
+};
+
+template <int P, bool RES_IN>
+__device__ __forceinline__ void split_load(const SplitArgs &a, int64_t base, int c,
+                                           ChunkIn<P, RES_IN> &in) {
 #pragma unroll
-  for (int p = 0; p < P; ++p) x[p] = load16(a.in.p[p] + base + c);
-  if constexpr (RES_IN) r = load16(a.res_in + base + c);
-  g = a.gamma[c];
-  hv = rank_order_sum<P>(x);
-  if constexpr (RES_IN) hv = add_bf16(hv, r);
+  for (int p = 0; p < P; ++p) in.x[p] = load16(a.in.p[p] + base + c);
+  if constexpr (RES_IN) in.r = load16(a.res_in + base + c);
+  in.g = a.gamma[c];
+}
+
+// Forms h and fl32(h * g) from one chunk's loads, and adds the chunk's share
+// of the statistics when `valid`.
+template <int P, bool RES_IN>
+__device__ __forceinline__ void split_chunk(const SplitArgs &a, const ChunkIn<P, RES_IN> &in,
+                                            bool valid, u32x4 &hv, float hg[8], float &ss,
+                                            float &mx) {
+  hv = rank_order_sum<P>(in.x);
+  if constexpr (RES_IN) hv = add_bf16(hv, in.r);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    gain2(hv[w], g[w], a.woff, hg[2 * w], hg[2 * w + 1]);
+    gain2(hv[w], in.g[w], a.woff, hg[2 * w], hg[2 * w + 1]);
     if (valid) {
       const float h0 = bf16_lo(hv[w]), h1 = bf16_hi(hv[w]);
       ss += h0 * h0;
@@ -116,11 +127,15 @@ __global__ __launch_bounds__(1024) void arnfp8_split_kernel(SplitArgs a) {
   const int first = part * a.cpp;
   const bool valid = t < a.cpp && first + t <= last;
   const int c = min(first + t, last);
+  ChunkIn<P, RES_IN> in;
+  split_load<P, RES_IN>(a, base, c, in);
+  // Every load is issued before any is consumed (s_setprio orders the
+  // scheduler as well as the wave).
+  __builtin_amdgcn_s_setprio(3);
   u32x4 hv;
   float hg[8];
   float ss = 0.0f, mx = 0.0f;
-  split_chunk<P, RES_IN>(a, base, c, valid, hv, hg, ss, mx);
-  __builtin_amdgcn_s_setprio(3);
+  split_chunk<P, RES_IN>(a, in, valid, hv, hg, ss, mx);
   const __amdgpu_buffer_rsrc_t rout =
       row_rsrc(RES_OUT ? (const void *)(a.res_out + base) : (const void *)a.gamma,
                RES_OUT ? a.c16 * 16 : 0);
@@ -181,10 +196,13 @@ __global__ __launch_bounds__(1024) void arnfp8_split_kernel(SplitArgs a) {
     if (missing[j]) {  // workgroup-uniform: read from LDS after a barrier
       const int fj = j * a.cpp;
       const bool vj = t < a.cpp && fj + t <= last;
+      ChunkIn<P, RES_IN> inj;
+      split_load<P, RES_IN>(a, base, min(fj + t, last), inj);
+      __builtin_amdgcn_sched_barrier(0);
       u32x4 hvj;
       float hgj[8];
       float ssj = 0.0f, mxj = 0.0f;
-      split_chunk<P, RES_IN>(a, base, min(fj + t, last), vj, hvj, hgj, ssj, mxj);
+      split_chunk<P, RES_IN>(a, inj, vj, hvj, hgj, ssj, mxj);
       float tj, mj;
       block_pair(ssj, mxj, red, slot, wave, nwaves, tj, mj);
       slot ^= 1;
