@@ -22,7 +22,8 @@ __all__ = [
     "library", "library_path", "VARIANT_AUTO", "VARIANT_ROW", "arnfp8_stage_bytes",
     "arnfp8_run_share", "SIMD_WIDTH", "arnfp8_run_fmt", "FMT_E4M3FN", "FMT_E5M2", "FMT_MXFP8",
     "CVT_BF16", "arnfp8_convert_f32", "STORES_AUTO", "STORES_NT", "STORES_SC1",
-    "SplitOpts", "arnfp8_split_workspace_bytes", "arnfp8_run_split", "arnfp8_run_split_noalloc",
+    "SplitOpts", "arnfp8_split_workspace_bytes", "arnfp8_split_parts", "arnfp8_run_split",
+    "arnfp8_run_split_noalloc",
     "NOALLOC_MAX_ROWS",
 ]
 
@@ -114,6 +115,8 @@ def library() -> ctypes.CDLL:
                                        ctypes.c_int, ctypes.c_int, vp]
         L.arnfp8_split_workspace_bytes.restype = ctypes.c_int64
         L.arnfp8_split_workspace_bytes.argtypes = [i64]
+        L.arnfp8_split_parts.restype = ctypes.c_int
+        L.arnfp8_split_parts.argtypes = [i64, i64]
         L.arnfp8_run_split.restype = ctypes.c_int
         L.arnfp8_run_split.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp, ctypes.c_float,
                                        ctypes.c_float, ctypes.c_float, i64, i64, ctypes.c_int,
@@ -306,6 +309,12 @@ def arnfp8_run_fmt(inputs, residual_in, residual_out, out_fp8, scales, gamma, ep
 def arnfp8_split_workspace_bytes(rows: int) -> int:
     """Bytes of the workspace ``arnfp8_run_split`` needs for ``rows`` rows (-1 if invalid)."""
     return int(library().arnfp8_split_workspace_bytes(int(rows)))
+
+
+def arnfp8_split_parts(rows, cols) -> int:
+    """Parts per row ``arnfp8_run_split`` picks automatically on the current
+    device for ``rows`` x ``cols`` (-1 if the shape is not valid)."""
+    return int(library().arnfp8_split_parts(int(rows), int(cols)))
 
 
 def arnfp8_run_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,

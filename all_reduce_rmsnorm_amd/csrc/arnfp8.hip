@@ -410,6 +410,21 @@ extern "C" int64_t arnfp8_split_workspace_bytes(int64_t rows) {
 
 namespace {
 
+// The largest power of two up to kSplitSlots that keeps the grid within one
+// workgroup per CU and every part at least one full wave of chunks, and at
+// least enough parts for 1024 lanes.  Measured on MI355X (graph replay,
+// inputs out of cache): one row of 8192 columns, P = 8, in 8 parts 4.71
+// against 5.89 us in one workgroup; 128 rows in 2 parts 7.40 against 7.77 us;
+// 4 rows of 256 columns in 8 parts of 4 chunks 5.76 against 2.89 us (the
+// exchange is then all overhead).
+int auto_split_parts(int64_t rows, int c16) {
+  const int64_t cus = device_cus();
+  int parts = 1;
+  while (parts * 2 <= kSplitSlots && rows * parts * 2 <= cus && c16 >= 64 * parts * 2) parts *= 2;
+  while (c16 > 1024 * parts && parts < kSplitSlots) parts *= 2;
+  return parts;
+}
+
 // A validated split call: the kernel, its arguments and its launch shape;
 // with one part per row, the row kernel of arnfp8_run instead.
 struct SplitCall {
@@ -484,17 +499,7 @@ int prepare_split(const void *const *inputs, const void *residual_in, void *resi
       return ARNFP8_ALIAS;
   }
   if (parts == 0) {
-    // The largest power of two up to kSplitSlots that keeps the grid within
-    // one workgroup per CU and every part at least one full wave of chunks,
-    // and at least enough parts for 1024 lanes.  Measured on MI355X (graph
-    // replay, inputs out of cache): one row of 8192 columns, P = 8, in 8
-    // parts 4.71 against 5.89 us in one workgroup; 128 rows in 2 parts 7.40
-    // against 7.77 us; 4 rows of 256 columns in 8 parts of 4 chunks 5.76
-    // against 2.89 us (the exchange is then all overhead).
-    const int64_t cus = device_cus();
-    parts = 1;
-    while (parts * 2 <= kSplitSlots && rows * parts * 2 <= cus && c16 >= 64 * parts * 2) parts *= 2;
-    while (c16 > 1024 * parts && parts < kSplitSlots) parts *= 2;
+    parts = auto_split_parts(rows, c16);
     if (c16 > 1024 * parts) return ARNFP8_BAD_CONFIG;
   }
   if (parts == 1) {
@@ -520,6 +525,13 @@ int prepare_split(const void *const *inputs, const void *residual_in, void *resi
 }
 
 }  // namespace
+
+extern "C" int arnfp8_split_parts(int64_t rows, int64_t cols) {
+  if (check_shape(rows, cols, 1) != ARNFP8_OK || rows == 0) return -1;
+  const int c16 = (int)(cols / 8);
+  const int parts = auto_split_parts(rows, c16);
+  return c16 > 1024 * parts ? -1 : parts;
+}
 
 extern "C" int arnfp8_run_split(const void *const *inputs, const void *residual_in,
                                 void *residual_out, void *out_fp8, float *scales,

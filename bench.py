@@ -236,14 +236,9 @@ def split_call_on(w, d, arn, workspace):
                                         w.scale_ub, workspace=workspace)
 
 
-def split_parts(w, cus):
-    """The automatic parts per row of arnfp8_run_split (for the record)."""
-    parts = 1
-    while parts * 2 <= 8 and w.rows * parts * 2 <= cus and w.cols // 8 >= 64 * parts * 2:
-        parts *= 2
-    while w.cols // 8 > 1024 * parts and parts < 8:
-        parts *= 2
-    return parts
+def split_parts(w, arn):
+    """The parts per row arnfp8_run_split picks for workload `w` (for the record)."""
+    return arn.arnfp8_split_parts(w.rows, w.cols)
 
 
 def step_fn(w, d, arn):
@@ -362,7 +357,7 @@ def latency_figures(w, torch, arn, dev, flush, khash, calls=100, nwin=64):
         ws = torch.zeros((arn.arnfp8_split_workspace_bytes(w.rows) // 8,), dtype=torch.int64,
                          device=dev)
         fsp = [split_call_on(w, d, arn, ws) for d in wins]
-        r["split_parts"] = split_parts(w, torch.cuda.get_device_properties(dev).multi_processor_count)
+        r["split_parts"] = split_parts(w, arn)
         r["split_warm_us_per_call"] = round(graph_us_per_call(torch, [fsp[0]] * calls), 3)
         r["split_cold_us_per_call"] = round(graph_us_per_call(torch, fsp, flush=flush), 3)
         sk_us = read_profile(profile_path(w.name, "kernel_trace", True), "mean_us", khash)

@@ -274,6 +274,12 @@ typedef struct arnfp8_split_opts {
   int spin_polls;
 } arnfp8_split_opts;
 
+/* The parts per row arnfp8_run_split picks when opt is NULL or opt->parts is 0,
+ * on the current device (its compute-unit count), for rows x cols: 1..8, or -1
+ * when rows <= 0 or cols is not a valid width.  Queries the device only for
+ * its compute-unit count (256 is assumed when no device can be queried). */
+int arnfp8_split_parts(int64_t rows, int64_t cols);
+
 /* Workspace bytes arnfp8_run_split needs for `rows` rows (128 per row), or -1
  * for rows < 0. */
 int64_t arnfp8_split_workspace_bytes(int64_t rows);

@@ -377,3 +377,29 @@ def test_noalloc_split_refuses_before_touching_the_device(L):
     assert noalloc(0) == OK
     assert noalloc(0, eps=-1.0) == BAD_SCALAR
     assert noalloc(0, parts=9) == 7
+
+
+def test_split_parts_rule_without_a_device(L):
+    """The automatic part count: the largest power of two up to 8 with rows x
+    parts within the compute units (256 assumed when no device answers) and
+    at least 64 chunks per part, and enough parts for 1024 lanes each."""
+    import all_reduce_rmsnorm_amd as arn
+
+    try:
+        import torch
+
+        if torch.cuda.is_available():
+            pytest.skip("the device's own compute-unit count applies")
+    except ImportError:
+        pass
+    assert arn.arnfp8_split_parts(1, 8192) == 8
+    assert arn.arnfp8_split_parts(1, 7168) == 8        # 896 chunks: 8 parts of 112
+    assert arn.arnfp8_split_parts(32, 7168) == 8
+    assert arn.arnfp8_split_parts(64, 7168) == 4
+    assert arn.arnfp8_split_parts(128, 8192) == 2
+    assert arn.arnfp8_split_parts(300, 7168) == 1
+    assert arn.arnfp8_split_parts(4, 256) == 1         # 32 chunks: under one wave per part
+    assert arn.arnfp8_split_parts(1, 1024) == 2        # 128 chunks: two parts of 64
+    assert arn.arnfp8_split_parts(1000, 65536) == 8    # 8192 chunks need 8 parts of 1024
+    assert arn.arnfp8_split_parts(0, 256) == -1
+    assert arn.arnfp8_split_parts(4, 12) == -1
