@@ -26,7 +26,9 @@
 //    slot s, part 0 also the slots past the last part), so the slots of a
 //    row always agree, whatever the shapes of earlier launches; a part reads
 //    its own slot's count before publishing to learn this launch's count.
-//    No host-side epoch is needed, and graph replays stay in step.
+//    No host-side epoch is needed, and graph replays stay in step.  (A call
+//    with one part per row launches the row kernel instead and leaves the
+//    counts as they are.)
 //  * The wait is bounded.  A part whose partner has not published when the
 //    bound runs out computes that partner's pair itself, from the inputs,
 //    with the partner's own lanes, chunk order and reductions, so the pair is
