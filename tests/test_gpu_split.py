@@ -219,3 +219,35 @@ def test_one_part_runs_the_row_kernel(arn, rows, cols, P, parts):
     for u, v in zip(got, (out, sc, ro)):
         assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
     assert torch.all(ws == 77)
+
+
+def test_two_streams_with_their_own_workspaces(arn):
+    """Split calls running at the same time on two streams, each with its own
+    workspace, give the bits of the same calls run one after the other."""
+    rows, cols, P = 16, 8192, 8
+    cases = [_case(41 + k, rows, cols, P, "in_out") for k in range(2)]
+    dev_cases = [([x.to(DEV) for x in xs], res.to(DEV), g.to(DEV)) for xs, res, g in cases]
+    wss = [_workspace(arn, rows) for _ in range(2)]
+    outs = [(torch.empty((rows, cols), dtype=torch.uint8, device=DEV),
+             torch.empty((rows,), dtype=torch.float32, device=DEV),
+             torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV)) for _ in range(2)]
+    seq = []
+    for (xs, res, g), ws in zip(dev_cases, wss):
+        o = (torch.empty((rows, cols), dtype=torch.uint8, device=DEV),
+             torch.empty((rows,), dtype=torch.float32, device=DEV),
+             torch.empty((rows, cols), dtype=torch.bfloat16, device=DEV))
+        arn.arnfp8_run_split(xs, res, o[2], o[0], o[1], g, 1e-6, 0.0, 1200.0, workspace=ws)
+        torch.cuda.synchronize()
+        seq.append(o)
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(10):
+        for (xs, res, g), ws, o, s in zip(dev_cases, wss, outs, streams):
+            with torch.cuda.stream(s):
+                arn.arnfp8_run_split(xs, res, o[2], o[0], o[1], g, 1e-6, 0.0, 1200.0,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    for o, want in zip(outs, seq):
+        for u, v in zip(o, want):
+            assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))

@@ -109,3 +109,36 @@ def test_noalloc_refuses_rows_beyond_the_limit(arn):
                                       cols, 1, None, None) == 0
     torch.cuda.synchronize()
     assert torch.all(out == 0x11) and torch.all(sc == -1.0)
+
+
+def test_noalloc_in_a_graph_matches_eager(arn):
+    """An allocation-free call captured in a graph (after eager calls on the
+    device): every replay, with eager work and synchronisations between
+    replays, equals the eager result bit for bit."""
+    rows, cols, P = 8, 8192, 8
+    xs, res, gamma = _case(123, rows, cols, P)
+    o = _outputs(rows, cols)
+
+    def call():
+        arn.arnfp8_run_split_noalloc(xs, res, o[2], o[0], o[1], gamma, 1e-6, 0.0, 1200.0)
+
+    call()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in o]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for k in range(3):
+        o[0].fill_(0x7F)
+        o[1].fill_(-1.0)
+        o[2].fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert _same(o, eager), k
+        _ = (xs[0].float() * 3.0).sum().item()
