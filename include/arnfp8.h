@@ -31,9 +31,11 @@
  *     and its P pointers are passed by value to the kernel; the caller may
  *     reuse the array as soon as the call returns.
  *   - Ownership: the caller owns every buffer.  The library allocates nothing
- *     and keeps no state between calls (beyond a cached compute-unit count per
- *     device), so calls may be captured in a HIP graph; pointers captured that
- *     way must stay valid for the graph's life.
+ *     and keeps no state between calls beyond a cached compute-unit count per
+ *     device and the split path's per-row counts (in the caller's workspace,
+ *     or in the library's own array for arnfp8_run_split_noalloc), so calls
+ *     may be captured in a HIP graph; pointers captured that way must stay
+ *     valid for the graph's life.
  *   - Validation happens on the host before any launch and touches no device
  *     state; a call that returns an error has launched nothing.
  *   - Execution is asynchronous on `stream` (NULL = the default stream);
@@ -41,7 +43,8 @@
  *     deterministic: bitwise identical on every call with the same arguments
  *     (the automatic launch shape depends only on rows, cols, P and the
  *     device), including calls replayed from a captured graph.
- *   - Concurrent calls on different streams must not share output buffers.
+ *   - Concurrent calls on different streams must not share output buffers
+ *     (nor, on the split path, a workspace).
  *   - Non-finite inputs are not supported (the results are unspecified), nor
  *     are rows whose sum of squares leaves the fp32 range (|h| of order 1e18
  *     and above): the row statistics are fp32.

@@ -512,7 +512,7 @@ def test_graph_replay_of_share_and_formats(arn, synth):
 
 
 def test_concurrent_calls_on_two_streams(arn, synth):
-    """The library keeps no state between calls: two streams running the fused
+    """arnfp8_run keeps no state between calls: two streams running the fused
     op at the same time, each on its own buffers, give the single-stream
     results bit for bit."""
     w = synth.WORKLOADS["unit_offset_p8_128x8192"]
