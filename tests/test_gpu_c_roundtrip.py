@@ -33,7 +33,7 @@ def build_roundtrip(out_path):
 def test_c_program_round_trip(tmp_path):
     exe = tmp_path / "gpu_roundtrip"
     build_roundtrip(exe)
-    print("[c] gpu_roundtrip 37 x 7176, P = 5", flush=True)
+    print("[c] gpu_roundtrip 37 x 7176, P = 5: fused, sum, split, allocation-free split", flush=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "gpu_roundtrip: ok" in r.stdout
