@@ -442,11 +442,14 @@ int launch_split(const SplitCall &c, hipStream_t stream) {
 
 // Validates a split call in the documented order and fills `call`.  Returns
 // ARNFP8_OK with neither kernel set when there is nothing to launch (rows ==
-// 0); the workspace is only looked at when there is.
+// 0); the workspace is only looked at when there is.  With `own_workspace`
+// the workspace is the library's array, set by the caller afterwards, and is
+// not checked.
 int prepare_split(const void *const *inputs, const void *residual_in, void *residual_out,
                   void *out_fp8, float *scales, const void *gamma, float eps, float weight_offset,
                   float scale_ub, int64_t rows, int64_t cols, int P, void *workspace,
-                  int64_t workspace_bytes, const arnfp8_split_opts *opt, SplitCall *call) {
+                  int64_t workspace_bytes, const arnfp8_split_opts *opt, SplitCall *call,
+                  bool own_workspace = false) {
   call->kernel = nullptr;
   call->row_kernel = nullptr;
   int st = check_shape(rows, cols, P);
@@ -480,11 +483,11 @@ int prepare_split(const void *const *inputs, const void *residual_in, void *resi
     a.rows = r.rows;
     a.c16 = r.c16;
   }
-  if (workspace == nullptr) return ARNFP8_NULL_POINTER;
-  if (!aligned(workspace, 16)) return ARNFP8_MISALIGNED;
   const int64_t need = arnfp8_split_workspace_bytes(rows);
-  if (need < 0 || workspace_bytes < need) return ARNFP8_BAD_WORKSPACE;
-  {
+  if (!own_workspace) {
+    if (workspace == nullptr) return ARNFP8_NULL_POINTER;
+    if (!aligned(workspace, 16)) return ARNFP8_MISALIGNED;
+    if (need < 0 || workspace_bytes < need) return ARNFP8_BAD_WORKSPACE;
     const Range ws{(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)need};
     const uintptr_t n = (uintptr_t)(rows * cols);
     for (int p = 0; p < P; ++p)
@@ -604,19 +607,19 @@ extern "C" int arnfp8_run_split_noalloc(const void *const *inputs, const void *r
   int st = check_shape(rows, cols, P);
   if (st != ARNFP8_OK) return st;
   if (rows > ARNFP8_NOALLOC_MAX_ROWS) return ARNFP8_BAD_WORKSPACE;
+  // Every check first; the array is looked up only for a launch that uses it.
   SplitCall c;
-  if (rows == 0)  // validation only; nothing is launched and no device is touched
-    return prepare_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
-                         weight_offset, scale_ub, rows, cols, P, nullptr, 0, opt, &c);
+  st = prepare_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
+                     weight_offset, scale_ub, rows, cols, P, nullptr, 0, opt, &c, true);
+  if (st != ARNFP8_OK) return st;
+  if (c.kernel == nullptr) {  // rows == 0, or one part per row (the row kernel)
+    return c.row_kernel == nullptr ? ARNFP8_OK : launch_split(c, stream);
+  }
   int dev = 0;
   unsigned long long *ws = nullptr;
   st = scratch_for_current_device(&dev, &ws);
   if (st != ARNFP8_OK) return st;
-  st = prepare_split(inputs, residual_in, residual_out, out_fp8, scales, gamma, eps,
-                     weight_offset, scale_ub, rows, cols, P, ws,
-                     kScratchWords * (int64_t)sizeof(unsigned long long), opt, &c);
-  if (st != ARNFP8_OK) return st;
-  if (c.row_kernel != nullptr) return launch_split(c, stream);  // the array is not used
+  c.args.ws = ws;
   if (!scratch_cleared[dev].load(std::memory_order_acquire)) {
     // The per-row counts must start equal: clear the whole array once, ahead
     // of the first launch on this device.  Under graph capture (or if the

@@ -304,9 +304,11 @@ int arnfp8_run_split(const void *const *inputs, const void *residual_in, void *r
  *   rows       at most ARNFP8_NOALLOC_MAX_ROWS, else ARNFP8_BAD_WORKSPACE
  *              (checked after the shape, before everything else)
  *   stream     a stream of the current device; the array used is that
- *              device's.  The first call with rows > 0 on a device looks the
- *              array's address up and clears the array on `stream`, before
- *              its own launch.
+ *              device's.  Every argument is validated first (no workspace
+ *              checks apply); the first call on a device that launches the
+ *              split kernel then looks the array's address up and clears the
+ *              array on `stream`, before its own launch.  A call with one part
+ *              per row runs arnfp8_run's kernel and does not use the array.
  * Every call on a device shares that device's array and leaves its per-row
  * counts for the next call, of any shape: calls that may run at the same time
  * on one device (other streams, other threads) race and give wrong results;

@@ -377,6 +377,18 @@ def test_noalloc_split_refuses_before_touching_the_device(L):
     assert noalloc(0) == OK
     assert noalloc(0, eps=-1.0) == BAD_SCALAR
     assert noalloc(0, parts=9) == 7
+    # rows > 0: every argument is checked before the library's array is looked up
+    assert noalloc(4, parts=9) == 7
+    assert noalloc(4, cols=65536, parts=1) == 7
+    assert L.arnfp8_run_split_noalloc(_arr(x0, x1), None, None, out, sc, None, 1e-6, 0.0, 1.0,
+                                      4, 256, 2, None, None) == NULLP
+    assert L.arnfp8_run_split_noalloc(_arr(x0, x1), None, None, out + 8, sc, g, 1e-6, 0.0, 1.0,
+                                      4, 256, 2, None, None) == MISALIGNED
+    r = BASE + 400 * MB
+    assert L.arnfp8_run_split_noalloc(_arr(x0, x1), r, r, out, sc, g, 1e-6, 0.0, 1.0,
+                                      4, 256, 2, None, None) == ALIAS
+    assert L.arnfp8_run_split_noalloc(_arr(x0, x1), None, x1, out, sc, g, 1e-6, 0.0, 1.0,
+                                      4, 256, 2, None, None) == ALIAS
 
 
 def test_split_parts_rule_without_a_device(L):
