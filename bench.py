@@ -17,7 +17,9 @@ outputs in cache.  Prints ONE JSON line:
               matches the current kernel source
   cpu_baseline the CPU oracle on the same bytes (rows of the same workload)
   two_stage_share  the 8 ranks' 1024-row shares of the same inputs, replayed
-              from a captured graph (no host launch cost), with its roofline
+              from a captured graph (no host launch cost), with its roofline,
+              and the reference kernels (read-only, traffic twin) at the
+              share's shape, timed the same way
   latency     per small workload (decode, unit offset, one token, tiny, sum):
               graph-replayed microseconds per call with the same buffers every
               call (cache-warm) and with every call on its own inputs after a
@@ -253,6 +255,45 @@ def share_calls(w, d, arn, staging):
                                               staging[r], d["gamma"], w.eps, w.weight_offset,
                                               w.scale_ub, ngpus=SHARE_NGPUS, rank=r))
             for r in range(SHARE_NGPUS)]
+
+
+def share_reference(w, d, torch, dev):
+    """The bench's reference kernels at one share's shape, timed as the share
+    is (the 8 ranks' row ranges in turn, four rounds in one graph): reading
+    the share's 9 streams, and the traffic twin (the same reads plus 16 + 8
+    bytes written per 16-byte chunk, no arithmetic)."""
+    import ctypes
+
+    L = ref_library()
+    S = -(-w.rows // SHARE_NGPUS)
+    streams = list(d["inputs"]) + [d["residual"]]
+    arrs = [(ctypes.c_void_p * len(streams))(*[t[r * S:(r + 1) * S].data_ptr() for t in streams])
+            for r in range(SHARE_NGPUS)]
+    sink = torch.empty((S, 16), dtype=torch.uint8, device=dev)
+    tw16 = [torch.empty((S, w.cols), dtype=torch.bfloat16, device=dev) for _ in range(SHARE_NGPUS)]
+    tw8 = [torch.empty((S, w.cols), dtype=torch.uint8, device=dev) for _ in range(SHARE_NGPUS)]
+
+    def checked(st):
+        if st != 0:
+            raise RuntimeError(f"reference kernel launch failed with status {st}")
+
+    def stream():
+        return torch.cuda.current_stream().cuda_stream
+
+    read = [(lambda r=r: checked(L.arnref_read(arrs[r], len(streams), sink.data_ptr(), S,
+                                               2 * w.cols, 0, 0, stream())))
+            for r in range(SHARE_NGPUS)]
+    twin = [(lambda r=r: checked(L.arnref_twin(arrs[r], len(streams), tw16[r].data_ptr(),
+                                               tw8[r].data_ptr(), S, 2 * w.cols, 0, 0, stream())))
+            for r in range(SHARE_NGPUS)]
+    rd_us = graph_us_per_call(torch, read * 4, reps=7)
+    tw_us = graph_us_per_call(torch, twin * 4, reps=7)
+    rd_bytes = len(streams) * 2 * S * w.cols
+    tw_bytes = rd_bytes + 3 * S * w.cols
+    return {"read_only_us": round(rd_us, 3),
+            "read_only_frac": round(rd_bytes / (rd_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic_twin_us": round(tw_us, 3),
+            "traffic_twin_frac": round(tw_bytes / (tw_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def share_bytes(w) -> int:
@@ -1078,6 +1119,7 @@ def main():
                 "traffic": read_profile(profile_path(SHARE_WORKLOAD, "hbm_traffic"),
                                         "traffic_bytes_per_launch", khash)},
         }
+        result["two_stage_share"]["reference_kernels"] = share_reference(w, d, torch, dev)
         log(f"bench: two-stage share {result['two_stage_share']}")
         del stg, calls
         result["reference_kernels"] = reference_kernels(w, d, torch, arn, dev, s_bufs)
