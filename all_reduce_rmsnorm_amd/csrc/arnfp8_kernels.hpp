@@ -185,10 +185,27 @@ constexpr int kDppQuadXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// A lane whose partner is inactive reads 0 (bound_ctrl): the identity of
+// every reduction below, whose operands are sums of squares and magnitudes.
+// An identity there lets the compiler fold the move into the consuming
+// add or max (one DPP instruction instead of a copy, a move and the op).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  const int x = __builtin_bit_cast(int, v);
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false));
+  return __uint_as_float(dpp_u<CTRL>(__float_as_uint(v)));
+}
+
+// The larger of two non-negative finite floats, compared as their bit
+// patterns (for such values the unsigned order of the patterns is the order
+// of the values): an integer max, which needs none of the NaN-quieting moves
+// the compiler puts ahead of a float max whose operands it cannot prove
+// canonical (values read from LDS or moved across lanes).
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ float max_nonneg(float a, float b) {
+  return __uint_as_float(umax(__float_as_uint(a), __float_as_uint(b)));
 }
 
 // Pairs across rows with gfx950's lane-swap moves (VALU, no LDS round trip).
@@ -226,15 +243,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   p = pair32(v);
   return p.x + p.y;
 }
+// The maximum of non-negative finite values (magnitudes), on their bit
+// patterns.
 __device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<kDppQuadXor1>(v));
-  v = fmaxf(v, dpp<kDppQuadXor2>(v));
-  v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp<kDppMirror>(v));
-  f32x2 p = pair16(v);
-  v = fmaxf(p.x, p.y);
-  p = pair32(v);
-  return fmaxf(p.x, p.y);
+  uint32_t u = __float_as_uint(v);
+  u = umax(u, dpp_u<kDppQuadXor1>(u));
+  u = umax(u, dpp_u<kDppQuadXor2>(u));
+  u = umax(u, dpp_u<kDppHalfMirror>(u));
+  u = umax(u, dpp_u<kDppMirror>(u));
+  f32x2 p = pair16(__uint_as_float(u));
+  u = umax(__float_as_uint(p.x), __float_as_uint(p.y));
+  p = pair32(__uint_as_float(u));
+  return __uint_as_float(umax(__float_as_uint(p.x), __float_as_uint(p.y)));
 }
 
 // ---------------------------------------------------------------- kernels --
@@ -494,7 +514,7 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
     float tot = 0.0f, m = 0.0f;
     for (int w = 0; w < nwaves; ++w) {
       tot += red[parity][w][0];
-      m = fmaxf(m, red[parity][w][1]);
+      m = max_nonneg(m, red[parity][w][1]);
     }
 
     // The row scalars sit on every row's critical path, so r and 1/scale use
@@ -545,8 +565,8 @@ __global__ __launch_bounds__(VPT == 1 ? 1024 : 512) void arnfp8_row_kernel(RowAr
             y[e] = y[e] * r;
             bmax = fmaxf(bmax, fabsf(y[e]));
           }
-          bmax = fmaxf(bmax, dpp<kDppQuadXor1>(bmax));
-          bmax = fmaxf(bmax, dpp<kDppQuadXor2>(bmax));
+          bmax = max_nonneg(bmax, dpp<kDppQuadXor1>(bmax));
+          bmax = max_nonneg(bmax, dpp<kDppQuadXor2>(bmax));
           const int ex = mx_shared_exp(bmax);
 #pragma unroll
           for (int e = 0; e < 8; ++e)

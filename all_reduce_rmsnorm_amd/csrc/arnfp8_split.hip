@@ -92,7 +92,7 @@ __device__ __forceinline__ void block_pair(float ss, float mx, float (*red)[16][
   m = 0.0f;
   for (int w = 0; w < nwaves; ++w) {
     tot += red[slot][w][0];
-    m = fmaxf(m, red[slot][w][1]);
+    m = max_nonneg(m, red[slot][w][1]);
   }
 }
 
@@ -220,7 +220,7 @@ __global__ __launch_bounds__(1024) void arnfp8_split_kernel(SplitArgs a) {
   float tot = 0.0f, m = 0.0f;
   for (int j = 0; j < a.parts; ++j) {
     tot += part_ss[j];
-    m = fmaxf(m, part_mx[j]);
+    m = max_nonneg(m, part_mx[j]);
   }
   const float den = tot * a.inv_cols + a.eps;
   const float r = den > 0.0f ? __builtin_amdgcn_rsqf(den) : 0.0f;
