@@ -124,7 +124,8 @@ def library() -> ctypes.CDLL:
         L.arnfp8_run_split_noalloc.restype = ctypes.c_int
         L.arnfp8_run_split_noalloc.argtypes = [ctypes.POINTER(vp), vp, vp, vp, vp, vp,
                                                ctypes.c_float, ctypes.c_float, ctypes.c_float,
-                                               i64, i64, ctypes.c_int, vp, vp]
+                                               i64, i64, ctypes.c_int, vp,
+                                               ctypes.POINTER(SplitOpts)]
         L.arn_sum_bf16.restype = ctypes.c_int
         L.arn_sum_bf16.argtypes = [ctypes.POINTER(vp), vp, i64, i64, ctypes.c_int, vp]
         L.arnfp8_status_string.restype = ctypes.c_char_p

@@ -81,6 +81,24 @@ def test_committed_counter_summary_matches_the_device_code():
     assert bench.read_traffic(bench.kernel_source_hash()) is not None
 
 
+def test_every_committed_profile_matches_the_device_code():
+    """Every workload's committed kernel trace and counter summary (the row or
+    sum kernel for each workload the benchmark reports, the split kernel for
+    the workloads it times through arnfp8_run_split) was taken on the current
+    device code."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    h = bench.kernel_source_hash()
+    names = [bench.DEFAULT_WORKLOAD, bench.SHARE_WORKLOAD] + list(bench.LATENCY_WORKLOADS)
+    wanted = [(n, False) for n in names] + [(n, True) for n in bench.SPLIT_PROFILE_WORKLOADS]
+    for name, split in wanted:
+        trace = bench.profile_path(name, "kernel_trace", split)
+        traffic = bench.profile_path(name, "hbm_traffic", split)
+        assert bench.read_profile(trace, "mean_us", h) is not None, trace
+        assert bench.read_profile(traffic, "traffic_bytes_per_launch", h) is not None, traffic
+
+
 def test_summarize_pmc_scales_by_the_copy(tmp_path):
     sys.path.insert(0, ROOT)
     import bench
