@@ -17,9 +17,10 @@ outputs in cache.  Prints ONE JSON line:
               matches the current kernel source
   cpu_baseline the CPU oracle on the same bytes (rows of the same workload)
   two_stage_share  the 8 ranks' 1024-row shares of the same inputs, replayed
-              from a captured graph (no host launch cost), with its roofline,
-              and the reference kernels (read-only, traffic twin) at the
-              share's shape, timed the same way
+              from a captured graph (no host launch cost), with its roofline;
+              the same with the residual updated in place; and the reference
+              kernels (read-only, traffic twin) at the share's shape, timed
+              the same way
   latency     per small workload (decode, unit offset, one token, tiny, sum):
               graph-replayed microseconds per call with the same buffers every
               call (cache-warm) and with every call on its own inputs after a
@@ -248,12 +249,15 @@ def step_fn(w, d, arn):
     return rotating([call_on(w, dict(d, **o), arn) for o in d["outs"]])
 
 
-def share_calls(w, d, arn, staging):
+def share_calls(w, d, arn, staging, residual=None):
     """The SHARE_NGPUS ranks' two-stage shares of the prefill inputs `d`, each
-    into its own staging slot, the residual rows written into d["res_out"]."""
-    return [(lambda r=r: arn.arnfp8_run_share(d["inputs"], d["residual"], d["res_out"],
-                                              staging[r], d["gamma"], w.eps, w.weight_offset,
-                                              w.scale_ub, ngpus=SHARE_NGPUS, rank=r))
+    into its own staging slot, the residual rows written into d["res_out"]
+    (or, with `residual`, read from and written back into that tensor)."""
+    res_in = d["residual"] if residual is None else residual
+    res_out = d["res_out"] if residual is None else residual
+    return [(lambda r=r: arn.arnfp8_run_share(d["inputs"], res_in, res_out, staging[r],
+                                              d["gamma"], w.eps, w.weight_offset, w.scale_ub,
+                                              ngpus=SHARE_NGPUS, rank=r))
             for r in range(SHARE_NGPUS)]
 
 
@@ -1119,6 +1123,14 @@ def main():
                 "traffic": read_profile(profile_path(SHARE_WORKLOAD, "hbm_traffic"),
                                         "traffic_bytes_per_launch", khash)},
         }
+        # The same shares with the residual updated in place (a copy of the
+        # residual, so that the other measurements keep their inputs).
+        res_copy = d["residual"].clone()
+        sh_in_place = graph_us_per_call(torch, share_calls(w, d, arn, stg, res_copy) * 4, reps=7)
+        del res_copy
+        result["two_stage_share"]["in_place_residual"] = {
+            "graph_us_per_call": round(sh_in_place, 3),
+            "frac": round(sb / (sh_in_place * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         result["two_stage_share"]["reference_kernels"] = share_reference(w, d, torch, dev)
         log(f"bench: two-stage share {result['two_stage_share']}")
         del stg, calls
