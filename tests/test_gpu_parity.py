@@ -441,6 +441,40 @@ def test_two_stage_share_and_staging_layout(arn, orc, ngpus):
         assert np.array_equal(sc_g, full[1].cpu().numpy()[first:first + count])
 
 
+def test_two_stage_share_in_place(arn):
+    """Every rank's share with the residual updated in place (residual_out ==
+    residual_in, as the benchmark also times it): the slot and the share's
+    residual rows are the out-of-place share's bits, and rows outside the
+    share keep their input values."""
+    rows, cols, P, ngpus = 37, 2880, 4, 8
+    print(f"[share] in place ngpus={ngpus}", flush=True)
+    g = torch.Generator().manual_seed(55)
+    dxs = [(torch.randn((rows, cols), generator=g) * 0.5).to(torch.bfloat16).to(DEV)
+           for _ in range(P)]
+    res = torch.randn((rows, cols), generator=g).to(torch.bfloat16).to(DEV)
+    gamma = (torch.rand((cols,), generator=g) * 0.4 + 0.8).to(torch.bfloat16).to(DEV)
+    nbytes = arn.arnfp8_stage_bytes(rows, cols, ngpus)
+    S = -(-rows // ngpus)
+    for rank in range(ngpus):
+        want_slot = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+        want_res = torch.full((rows, cols), 7.0, dtype=torch.bfloat16, device=DEV)
+        arn.arnfp8_run_share(dxs, res, want_res, want_slot, gamma, 1e-6, 0.0, 1200.0,
+                             ngpus=ngpus, rank=rank)
+        slot = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+        inplace = res.clone()
+        arn.arnfp8_run_share(dxs, inplace, inplace, slot, gamma, 1e-6, 0.0, 1200.0,
+                             ngpus=ngpus, rank=rank)
+        torch.cuda.synchronize()
+        assert torch.equal(slot, want_slot), rank
+        first, last = rank * S, min(rows, (rank + 1) * S)
+        if first < last:
+            assert torch.equal(inplace[first:last].view(torch.int16),
+                               want_res[first:last].view(torch.int16)), rank
+        outside = torch.ones(rows, dtype=torch.bool, device=DEV)
+        outside[first:last] = False
+        assert torch.equal(inplace[outside].view(torch.int16), res[outside].view(torch.int16))
+
+
 def test_slabs_larger_than_4GiB(arn, orc):
     """64-bit offsets: P = 2 slabs of 4.3 GiB each (rows x cols x 2 bytes > 2^32);
     the oracle checks rows past the 4 GiB mark, and the sum kernel the same."""
