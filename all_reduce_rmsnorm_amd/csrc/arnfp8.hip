@@ -134,8 +134,10 @@ struct RowConfig {
 // lanes) is faster: measured (graph replay, inputs out of cache / the same
 // inputs every call) at 1 row 5.71 / 3.75 against 5.89 / 3.90 us for
 // 7168-wide rows and 5.84 / 3.75 against 6.08 / 3.89 us for 8192-wide rows,
-// and 2-3 % faster out of cache up to 256 rows.  With four slabs it is not
-// (1 row: 5.02 / 3.44 against 4.97 / 3.22 us).
+// and 2-3 % faster out of cache up to 256 rows.  With four slabs (7168
+// columns) it trades: 0.1-0.25 us faster out of cache and 0.08-0.16 us
+// slower with the inputs cache-warm, from 1 to 128 rows (32 rows: 5.26 /
+// 3.49 against 5.35 / 3.40 us); two chunks per lane are kept there.
 RowConfig pick_row_config(int64_t rows, int c16, int P) {
   static const int vpts[5] = {1, 2, 4, 8, 16};
   const int64_t cus = device_cus();
